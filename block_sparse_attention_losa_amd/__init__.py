@@ -1,0 +1,14 @@
+"""LoSA attention hot path on MI355X (gfx950): dense attention, block mass
+map, threshold selection and block-sparse attention over frozen block lists,
+as hand-written HIP kernels behind the C-ABI of ``include/losa.h``.
+
+The functions below are argument marshalling around ``liblosa.so``; they
+raise if the library has not been built (``python -m
+block_sparse_attention_losa_amd.build``).
+"""
+
+from ._lib import LosaError, LosaLibraryMissing  # noqa: F401
+from .api import block_mass, dense_attn, num_blocks, select, sparse_attn  # noqa: F401
+
+__all__ = ["dense_attn", "block_mass", "select", "sparse_attn", "num_blocks",
+           "LosaError", "LosaLibraryMissing"]

@@ -1,0 +1,130 @@
+"""Thin torch-facing binding of the C-ABI (same names as the C entry points).
+
+Only argument marshalling happens here: output tensors are allocated with
+``torch.empty`` on the inputs' device and every computation runs in the HIP
+kernels of ``liblosa.so``, enqueued on torch's current stream.
+"""
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.bfloat16: _lib.LOSA_BF16, torch.float32: _lib.LOSA_FP32}
+
+
+def num_blocks(seq_len: int, block: int) -> int:
+    return (int(seq_len) + int(block) - 1) // int(block)
+
+
+def make_desc(q: torch.Tensor, block: int, scale=None) -> _lib.AttnDesc:
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, D] tensors")
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    b, h, n, d = q.shape
+    return _lib.AttnDesc(b, h, n, d, int(block), _DTYPES[q.dtype],
+                         0.0 if scale is None else float(scale))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check_inputs(*ts):
+    ref = ts[0]
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on a GPU")
+        if t.device != ref.device:
+            raise ValueError("tensors must share one device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def dense_attn(q, k, v, block: int = 64, scale=None, o=None, lse=None, want_lse=True):
+    """Dense softmax attention; returns ``(o, lse)`` (lse None if not wanted)."""
+    _check_inputs(q, k, v)
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    desc = make_desc(q, block, scale)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    _lib.check("losa_dense_attn", lib.losa_dense_attn(
+        desc, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(q)))
+    return o, lse
+
+
+def block_mass(q, k, block: int = 64, lse=None, scale=None, mass=None, lse_scratch=None):
+    """Block mass map ``[B, H, nb, nb]`` (float32); runs the lse pass first
+    when ``lse`` is None."""
+    _check_inputs(q, k)
+    if k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("q, k must share shape and dtype")
+    desc = make_desc(q, block, scale)
+    b, h, n, _ = q.shape
+    nb = num_blocks(n, block)
+    if mass is None:
+        mass = torch.empty((b, h, nb, nb), dtype=torch.float32, device=q.device)
+    if lse is None and lse_scratch is None:
+        lse_scratch = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    _lib.check("losa_block_mass", lib.losa_block_mass(
+        desc, _ptr(q), _ptr(k), _ptr(lse), _ptr(lse_scratch), _ptr(mass), _stream(q)))
+    return mass
+
+
+def select(mass, threshold: float = 0.99, idx=None, count=None):
+    """Threshold selection over the last axis of ``mass``; returns
+    ``(idx, count)`` with idx shaped like mass (int32; entries at and past
+    count are left as allocated) and count shaped ``mass.shape[:-1]``."""
+    _check_inputs(mass)
+    if mass.dtype != torch.float32:
+        raise TypeError("mass must be float32")
+    nkb = mass.shape[-1]
+    rows = mass.numel() // nkb if nkb else 0
+    if idx is None:
+        idx = torch.empty(mass.shape, dtype=torch.int32, device=mass.device)
+    if count is None:
+        count = torch.empty(mass.shape[:-1], dtype=torch.int32, device=mass.device)
+    lib = _lib.load()
+    _lib.check("losa_select", lib.losa_select(
+        rows, nkb, _ptr(mass), float(threshold), _ptr(idx), _ptr(count), _stream(mass)))
+    return idx, count
+
+
+def sparse_attn(q, k, v, idx, count, block: int = 64, scale=None, o=None, lse=None,
+                want_lse=False):
+    """Block-sparse attention over frozen lists; returns ``(o, lse)``."""
+    _check_inputs(q, k, v, idx, count)
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    b, h, n, _ = q.shape
+    nb = num_blocks(n, block)
+    if tuple(idx.shape) != (b, h, nb, nb) or tuple(count.shape) != (b, h, nb):
+        raise ValueError("idx must be [B,H,nb,nb] and count [B,H,nb]")
+    if idx.dtype != torch.int32 or count.dtype != torch.int32:
+        raise TypeError("idx and count must be int32")
+    desc = make_desc(q, block, scale)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    _lib.check("losa_sparse_attn", lib.losa_sparse_attn(
+        desc, _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(count), _ptr(o), _ptr(lse),
+        _stream(q)))
+    return o, lse
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,149 @@
+// C-ABI of the LoSA hot path: argument validation and dispatch to the
+// kernels.  Every check happens before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/losa.h"
+#include "losa_launch.h"
+
+namespace {
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+losa_status check_desc(const losa_attn_desc* d, int32_t* nb_out) {
+  if (d == nullptr) return LOSA_ERR_NULL_POINTER;
+  if (d->dtype != LOSA_BF16 && d->dtype != LOSA_FP32) return LOSA_ERR_BAD_DTYPE;
+  if (d->batch < 1 || d->heads < 1 || d->seq_len < 1) return LOSA_ERR_BAD_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return LOSA_ERR_BAD_SHAPE;
+  if (d->block != 64 && d->block != 128) return LOSA_ERR_BAD_SHAPE;
+  const int64_t nb = (static_cast<int64_t>(d->seq_len) + d->block - 1) / d->block;
+  if (nb > LOSA_MAX_BLOCKS) return LOSA_ERR_BAD_SHAPE;
+  const int64_t items = static_cast<int64_t>(d->batch) * d->heads * nb;
+  if (items >= (int64_t{1} << 31)) return LOSA_ERR_BAD_SHAPE;
+  if (!std::isfinite(d->scale) || d->scale < 0.f) return LOSA_ERR_BAD_ARGUMENT;
+  *nb_out = static_cast<int32_t>(nb);
+  return LOSA_OK;
+}
+
+float effective_scale(const losa_attn_desc* d) {
+  return d->scale > 0.f ? d->scale : 1.0f / std::sqrt(static_cast<float>(d->head_dim));
+}
+
+losa::AttnParams base_params(const losa_attn_desc* d, int32_t nb) {
+  losa::AttnParams p{};
+  p.n = d->seq_len;
+  p.nb = nb;
+  p.items = d->batch * d->heads * nb;
+  p.scale = effective_scale(d);
+  return p;
+}
+
+losa_status device_status(hipError_t e) { return e == hipSuccess ? LOSA_OK : LOSA_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t losa_num_blocks(const losa_attn_desc* desc) {
+  if (desc == nullptr || desc->block < 1 || desc->seq_len < 0) return -1;
+  return static_cast<int32_t>((static_cast<int64_t>(desc->seq_len) + desc->block - 1) /
+                              desc->block);
+}
+
+losa_status losa_dense_attn(const losa_attn_desc* desc, const void* q, const void* k,
+                            const void* v, void* o, float* lse, void* stream) {
+  int32_t nb = 0;
+  losa_status st = check_desc(desc, &nb);
+  if (st != LOSA_OK) return st;
+  if (!q || !k || !v || !o) return LOSA_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)))
+    return LOSA_ERR_MISALIGNED;
+  losa::AttnParams p = base_params(desc, nb);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  return device_status(losa::launch_attn(losa::kDense, desc->dtype, desc->head_dim, desc->block,
+                                         p, static_cast<hipStream_t>(stream)));
+}
+
+losa_status losa_block_mass(const losa_attn_desc* desc, const void* q, const void* k,
+                            const float* lse, float* lse_scratch, float* mass, void* stream) {
+  int32_t nb = 0;
+  losa_status st = check_desc(desc, &nb);
+  if (st != LOSA_OK) return st;
+  if (!q || !k || !mass || (!lse && !lse_scratch)) return LOSA_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(mass, 4) || (lse && !aligned(lse, 4)) ||
+      (!lse && !aligned(lse_scratch, 4)))
+    return LOSA_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  losa::AttnParams p = base_params(desc, nb);
+  p.q = q;
+  p.k = k;
+  if (lse == nullptr) {
+    p.lse = lse_scratch;
+    st = device_status(
+        losa::launch_attn(losa::kLse, desc->dtype, desc->head_dim, desc->block, p, s));
+    if (st != LOSA_OK) return st;
+    lse = lse_scratch;
+  }
+  p.lse = nullptr;
+  p.lse_in = lse;
+  p.mass = mass;
+  return device_status(
+      losa::launch_attn(losa::kMass, desc->dtype, desc->head_dim, desc->block, p, s));
+}
+
+losa_status losa_select(int32_t rows, int32_t nkb, const float* mass, double threshold,
+                        int32_t* idx, int32_t* count, void* stream) {
+  if (!mass || !idx || !count) return LOSA_ERR_NULL_POINTER;
+  if (rows < 1 || nkb < 1 || nkb > LOSA_MAX_BLOCKS) return LOSA_ERR_BAD_SHAPE;
+  if (std::isnan(threshold) || !(threshold > 0.0)) return LOSA_ERR_BAD_THRESHOLD;
+  if (!aligned(mass, 4) || !aligned(idx, 4) || !aligned(count, 4)) return LOSA_ERR_MISALIGNED;
+  return device_status(
+      losa::launch_select(rows, nkb, mass, threshold, idx, count, static_cast<hipStream_t>(stream)));
+}
+
+losa_status losa_sparse_attn(const losa_attn_desc* desc, const void* q, const void* k,
+                             const void* v, const int32_t* idx, const int32_t* count, void* o,
+                             float* lse, void* stream) {
+  int32_t nb = 0;
+  losa_status st = check_desc(desc, &nb);
+  if (st != LOSA_OK) return st;
+  if (!q || !k || !v || !o || !idx || !count) return LOSA_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(idx, 4) || !aligned(count, 4) || (lse && !aligned(lse, 4)))
+    return LOSA_ERR_MISALIGNED;
+  losa::AttnParams p = base_params(desc, nb);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.idx = idx;
+  p.cnt = count;
+  p.o = o;
+  p.lse = lse;
+  return device_status(losa::launch_attn(losa::kSparse, desc->dtype, desc->head_dim, desc->block,
+                                         p, static_cast<hipStream_t>(stream)));
+}
+
+const char* losa_status_string(losa_status status) {
+  switch (status) {
+    case LOSA_OK: return "ok";
+    case LOSA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case LOSA_ERR_BAD_SHAPE: return "unsupported sizes (D, block, N, B*H*nb or nkb)";
+    case LOSA_ERR_BAD_DTYPE: return "unknown element type";
+    case LOSA_ERR_BAD_THRESHOLD: return "threshold must be > 0 and not NaN";
+    case LOSA_ERR_MISALIGNED: return "pointer alignment below the requirement";
+    case LOSA_ERR_DEVICE: return "the HIP runtime rejected a launch";
+    case LOSA_ERR_BAD_ARGUMENT: return "invalid argument (scale must be finite and >= 0)";
+  }
+  return "unknown status";
+}
+
+int32_t losa_version(void) { return 100; }
+
+}  // extern "C"

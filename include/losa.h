@@ -1,0 +1,142 @@
+/*
+ * losa.h -- C-ABI of the LoSA attention hot path for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * LoSA (arXiv 2608.12032) measures exact block attention masses at one early
+ * dense denoising step, keeps for every head and query block the smallest
+ * set of key/value blocks whose mass reaches a threshold (0.99 by default),
+ * and reuses those frozen block lists for block-sparse attention at every
+ * later step (mlsanity.com paper index, "Abstract (arXiv)"; legiblepapers,
+ * "Summary & Methodology Analysis" and FAQ Q4-Q6; ubos.tech blog, "How It
+ * Works in Practice", Phases 1-3).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors Q, K, V, O are contiguous [B, H, N, D] (D fastest) in device
+ *    memory, element type bf16 or fp32 (losa_dtype); they must be 16-byte
+ *    aligned.  lse is [B, H, N] fp32, natural log.  mass is [B, H, nb, nb]
+ *    fp32 (key block fastest); idx is [B, H, nb, nb] int32 and count
+ *    [B, H, nb] int32.  nb = ceil(N / block); the last block holds the
+ *    N - (nb-1)*block remaining tokens.  fp32/int32 arrays must be 4-byte
+ *    aligned.
+ *  - Every pointer argument is a device pointer owned by the caller; the
+ *    library never allocates, frees or synchronises, keeps no state between
+ *    calls and may be called from several host threads at once.  Outputs
+ *    must not overlap inputs.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    Work is enqueued asynchronously on it.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    status other than LOSA_OK means nothing was launched.  A launch the HIP
+ *    runtime rejects returns LOSA_ERR_DEVICE.  Faults while the kernels run
+ *    surface at the caller's next synchronisation, as for any HIP kernel.
+ *  - Limits: D in {64, 128}; block in {64, 128}; nb <= LOSA_MAX_BLOCKS;
+ *    B*H*nb < 2^31.
+ */
+#ifndef LOSA_H
+#define LOSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOSA_MAX_BLOCKS 1024
+
+typedef enum {
+  LOSA_OK = 0,
+  LOSA_ERR_NULL_POINTER = 1,   /* a required pointer is NULL                 */
+  LOSA_ERR_BAD_SHAPE = 2,      /* sizes outside the supported set           */
+  LOSA_ERR_BAD_DTYPE = 3,      /* unknown element type                      */
+  LOSA_ERR_BAD_THRESHOLD = 4,  /* threshold NaN or <= 0                     */
+  LOSA_ERR_MISALIGNED = 5,     /* pointer alignment below the requirement   */
+  LOSA_ERR_DEVICE = 6,         /* the HIP runtime rejected a launch         */
+  LOSA_ERR_BAD_ARGUMENT = 7    /* other invalid argument (e.g. scale)       */
+} losa_status;
+
+typedef enum { LOSA_BF16 = 0, LOSA_FP32 = 1 } losa_dtype;
+
+/* Shape of one attention layer call. */
+typedef struct {
+  int32_t batch;     /* B >= 1                                            */
+  int32_t heads;     /* H >= 1                                            */
+  int32_t seq_len;   /* N >= 1, tokens of the flattened 3D sequence       */
+  int32_t head_dim;  /* D, 64 or 128                                      */
+  int32_t block;     /* square block size (query and key), 64 or 128      */
+  int32_t dtype;     /* losa_dtype of Q, K, V and O                        */
+  float scale;       /* softmax scale c; 0 selects 1/sqrt(D)              */
+} losa_attn_desc;
+
+/* ceil(seq_len / block), or -1 when desc is NULL or block < 1. */
+int32_t losa_num_blocks(const losa_attn_desc* desc);
+
+/*
+ * Dense softmax attention over all N keys: the pass the sampler runs at its
+ * first denoising steps and at the construction step (legiblepapers,
+ * "Summary & Methodology Analysis"; mlsanity.com, "Abstract (arXiv)").
+ *   s_ij = c <q_i, k_j>,  lse_i = log sum_j exp(s_ij),
+ *   o_i  = sum_j exp(s_ij - lse_i) v_j.
+ * q, k, v: inputs [B,H,N,D]; o: output [B,H,N,D] (same dtype);
+ * lse: output [B,H,N] fp32, or NULL to skip it.
+ */
+losa_status losa_dense_attn(const losa_attn_desc* desc, const void* q, const void* k,
+                            const void* v, void* o, float* lse, void* stream);
+
+/*
+ * Exact block attention mass (the "mass map") of the construction step
+ * (mlsanity.com, "Abstract (arXiv)": exact block attention masses at one
+ * early dense step; ubos.tech blog, "How It Works in Practice", Phase 1):
+ *   M[b,h,I,J] = (1/|I|) sum_{i in I} sum_{j in J} exp(s_ij - lse_i)
+ * with |I| the valid rows of query block I.  Each row of M sums to 1.
+ * lse: the dense pass's row log-sum-exp [B,H,N]; when NULL, a first pass
+ *      computes it into lse_scratch ([B,H,N] fp32, then required).
+ * mass: output [B,H,nb,nb] fp32.
+ */
+losa_status losa_block_mass(const losa_attn_desc* desc, const void* q, const void* k,
+                            const float* lse, float* lse_scratch, float* mass,
+                            void* stream);
+
+/*
+ * Threshold selection (ubos.tech blog, "How It Works in Practice", Phase 2;
+ * mlsanity.com, "Abstract (arXiv)"; legiblepapers, FAQ Q4).  For each of the
+ * `rows` rows of `mass` ([rows, nkb] fp32, finite and >= 0): order the key
+ * blocks by descending mass, ties by ascending block index; accumulate the
+ * masses in that order in float64; count = the smallest k whose running sum
+ * reaches `threshold` (>=), or nkb when none does or threshold >= 1.
+ * idx: output [rows, nkb] int32; entries [0, count) hold the kept blocks in
+ *      that order, later entries are left untouched.
+ * count: output [rows] int32.
+ * Requires 1 <= nkb <= LOSA_MAX_BLOCKS, rows >= 1, threshold > 0 (not NaN).
+ * For the [B,H,nb,nb] mass map, rows = B*H*nb and nkb = nb.
+ */
+losa_status losa_select(int32_t rows, int32_t nkb, const float* mass, double threshold,
+                        int32_t* idx, int32_t* count, void* stream);
+
+/*
+ * Block-sparse attention over frozen block lists (ubos.tech blog, "How It
+ * Works in Practice", Phase 3; legiblepapers, "Summary & Methodology
+ * Analysis": later steps attend only to the retained keys).  For query
+ * block I of (b,h) the retained keys are the tokens of blocks
+ * idx[b,h,I,0:count[b,h,I]]; the softmax is renormalised over them:
+ *   lse'_i = log sum_{j kept} exp(s_ij),  o_i = sum_{j kept} exp(s_ij - lse'_i) v_j.
+ * idx/count as produced by losa_select; the lists may be in any order.
+ * Entries are trusted: each idx in [0, nb) (others are ignored), no
+ * duplicates needed, 1 <= count <= nb.  A query block whose list is empty
+ * gets o = 0 and lse' = -inf.
+ * o: output [B,H,N,D]; lse: output [B,H,N] fp32 or NULL.
+ */
+losa_status losa_sparse_attn(const losa_attn_desc* desc, const void* q, const void* k,
+                             const void* v, const int32_t* idx, const int32_t* count,
+                             void* o, float* lse, void* stream);
+
+/* Static text for a status code. */
+const char* losa_status_string(losa_status status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t losa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOSA_H */

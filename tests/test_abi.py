@@ -1,0 +1,108 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every entry point
+that include/losa.h declares, and rejects bad arguments before launching
+anything (no GPU needed: every call below fails validation on the host)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_losa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "losa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="liblosa.so not built")
+
+FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
+ODD = ctypes.c_void_p(0x10002)        # misaligned
+NULL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(losa_[a-z_]+)\s*\(", text)))
+
+
+def desc(**kw):
+    base = dict(batch=1, heads=2, seq_len=1000, head_dim=128, block=64, dtype=0, scale=0.0)
+    base.update(kw)
+    return _lib.AttnDesc(**base)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"losa_dense_attn", "losa_block_mass", "losa_select", "losa_sparse_attn"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of date"
+
+
+def test_status_strings_and_version(lib):
+    for code in range(8):
+        assert lib.losa_status_string(code)
+    assert lib.losa_status_string(99) == b"unknown status"
+    assert lib.losa_version() >= 100
+
+
+def test_num_blocks(lib):
+    assert lib.losa_num_blocks(desc(seq_len=32760, block=64)) == 512
+    assert lib.losa_num_blocks(desc(seq_len=118800, block=128)) == 929
+    assert lib.losa_num_blocks(desc(seq_len=64, block=64)) == 1
+    assert lib.losa_num_blocks(None) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), 2), (dict(block=32), 2), (dict(seq_len=0), 2), (dict(batch=0), 2),
+    (dict(heads=-1), 2), (dict(seq_len=1024 * 64 + 1), 2), (dict(dtype=5), 3),
+    (dict(scale=-1.0), 7), (dict(scale=float("nan")), 7), (dict(scale=float("inf")), 7),
+])
+def test_descriptor_validation(lib, kw, code):
+    d = desc(**kw)
+    assert lib.losa_dense_attn(d, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == code
+    assert lib.losa_sparse_attn(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == code
+    assert lib.losa_block_mass(d, FAKE, FAKE, FAKE, NULL, FAKE, NULL) == code
+
+
+def test_null_and_alignment(lib):
+    d = desc()
+    assert lib.losa_dense_attn(None, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == 1
+    assert lib.losa_dense_attn(d, NULL, FAKE, FAKE, FAKE, NULL, NULL) == 1
+    assert lib.losa_dense_attn(d, FAKE, FAKE, FAKE, NULL, NULL, NULL) == 1
+    assert lib.losa_dense_attn(d, ODD, FAKE, FAKE, FAKE, NULL, NULL) == 5
+    assert lib.losa_dense_attn(d, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10001), NULL) == 5
+    assert lib.losa_sparse_attn(d, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, NULL, NULL) == 1
+    assert lib.losa_sparse_attn(d, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, NULL, NULL) == 1
+    assert lib.losa_sparse_attn(d, FAKE, FAKE, ODD, FAKE, FAKE, FAKE, NULL, NULL) == 5
+    # block mass needs lse or a scratch buffer for the first pass
+    assert lib.losa_block_mass(d, FAKE, FAKE, NULL, NULL, FAKE, NULL) == 1
+    assert lib.losa_block_mass(d, FAKE, FAKE, FAKE, NULL, NULL, NULL) == 1
+    assert lib.losa_block_mass(d, FAKE, ODD, FAKE, NULL, FAKE, NULL) == 5
+
+
+@pytest.mark.parametrize("rows,nkb,tau,code", [
+    (0, 16, 0.99, 2), (4, 0, 0.99, 2), (4, 1025, 0.99, 2), (4, 16, 0.0, 4),
+    (4, 16, -0.5, 4), (4, 16, float("nan"), 4),
+])
+def test_select_validation(lib, rows, nkb, tau, code):
+    assert lib.losa_select(rows, nkb, FAKE, tau, FAKE, FAKE, NULL) == code
+
+
+def test_select_null_and_alignment(lib):
+    assert lib.losa_select(4, 16, NULL, 0.99, FAKE, FAKE, NULL) == 1
+    assert lib.losa_select(4, 16, FAKE, 0.99, NULL, FAKE, NULL) == 1
+    assert lib.losa_select(4, 16, FAKE, 0.99, FAKE, NULL, NULL) == 1
+    assert lib.losa_select(4, 16, ctypes.c_void_p(0x10001), 0.99, FAKE, FAKE, NULL) == 5
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(_lib.LosaLibraryMissing):
+        _lib.load(str(tmp_path / "missing.so"))

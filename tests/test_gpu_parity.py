@@ -1,0 +1,239 @@
+"""GPU parity of the HIP path against the fp64 oracle on small seeded inputs
+that span several tiles and ragged tails.
+
+Tolerances:
+  * masses: 1e-5 absolute (fp32 accumulation);
+  * attention outputs: 2e-2 max-abs and 2e-3 mean-abs (bf16 inputs and
+    outputs; the output rounding alone is up to 2^-9 relative);
+  * row log-sum-exp: 1e-3 absolute.  The logits are fp32 dot products of
+    exactly represented inputs; with |q.k| <= 512 and D = 128 products the
+    accumulated rounding is below 512 * 128 * 2^-24 ~ 4e-3 in the raw dot,
+    ~3.5e-4 after the 1/sqrt(128) scale, and the lse inherits at most that;
+  * selection: bit-identical counts and kept lists, the oracle deciding on
+    the GPU's own fp32 masses.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_losa_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+MASS_ATOL = 1e-5
+O_MAX = 2e-2
+O_MEAN = 2e-3
+LSE_ATOL = 1e-3
+TAUS = (0.5, 0.9, 0.95, 0.99, 0.999, 1.0)
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def losa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_losa_amd as mod
+    return mod
+
+
+def _dev(x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def _np(t):
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+CASES = {
+    "tiny-ref fp32": synth.CONFIGS[1],
+    "N105 D64 b64 bf16": synth.small_config(n_grid=(3, 5, 7), head_dim=64, block=64),
+    "N226 text D128 b64 B2H3": synth.small_config(n_grid=(4, 6, 9), text=10, heads=3, batch=2,
+                                                  head_dim=128, block=64,
+                                                  alpha=(4.0, 0.0, 2.0)),
+    "N264 D128 b128 tail8": synth.small_config(n_grid=(3, 8, 11), head_dim=128, block=128),
+    "N198 D64 b128 tail70": synth.small_config(n_grid=(2, 9, 11), head_dim=64, block=128),
+    "N1 D64": synth.small_config(n_grid=(1, 1, 1), head_dim=64, block=64, alpha=(1.0, 0.0)),
+    "N64 D128 exact": synth.small_config(n_grid=(2, 4, 8), head_dim=128, block=64),
+    "N128 D64 b128 exact": synth.small_config(n_grid=(2, 8, 8), head_dim=64, block=128),
+    "N1280 D128 b64 many tiles": synth.small_config(n_grid=(4, 16, 20), head_dim=128, block=64,
+                                                    heads=3, alpha=(3.0, 0.0, 1.5)),
+    "N700 fp32 D128 b128": synth.small_config(n_grid=(4, 7, 25), head_dim=128, block=128,
+                                              dtype="fp32", alpha=(2.5, 0.5)),
+    "N333 fp32 D64 b64": synth.small_config(n_grid=(3, 3, 37), head_dim=64, block=64,
+                                            dtype="fp32", alpha=(3.0, 1.0)),
+}
+
+
+def _compare_attention(o_gpu, lse_gpu, o_ref, lse_ref, what):
+    err = np.abs(o_gpu.astype(np.float64) - o_ref)
+    assert err.max() <= O_MAX, f"{what}: max-abs {err.max():.3e}"
+    assert err.mean() <= O_MEAN, f"{what}: mean-abs {err.mean():.3e}"
+    if lse_gpu is not None:
+        lerr = np.abs(lse_gpu.astype(np.float64) - lse_ref).max()
+        assert lerr <= LSE_ATOL, f"{what}: lse err {lerr:.3e}"
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_pipeline_matches_oracle(losa, name):
+    cfg = CASES[name]
+    _say(f"[parity] case {name}: N={cfg.seq_len} D={cfg.head_dim} block={cfg.block} {cfg.dtype}")
+    q, k, v = synth.make_inputs(cfg)
+    tq, tk, tv = (_dev(x, cfg.dtype) for x in (q, k, v))
+    blk = cfg.block
+    nb = cfg.num_blocks
+
+    _say(f"[parity] {name}: dense")
+    o, lse = losa.dense_attn(tq, tk, tv, block=blk)
+    _say(f"[parity] {name}: block_mass")
+    mass = losa.block_mass(tq, tk, block=blk, lse=lse)
+    mass_own = losa.block_mass(tq, tk, block=blk)  # first pass inside
+    torch.cuda.synchronize()
+    o_g, lse_g, mass_g = _np(o), _np(lse), _np(mass)
+    assert np.array_equal(mass_g, _np(mass_own)) or np.abs(mass_g - _np(mass_own)).max() < 1e-7
+
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            od, lsed = oracle.dense_attention(q[b, h], k[b, h], v[b, h])
+            _compare_attention(o_g[b, h], lse_g[b, h], od, lsed, f"{name} dense b{b}h{h}")
+            md = oracle.block_mass(q[b, h], k[b, h], blk, lse=lsed)
+            merr = np.abs(mass_g[b, h].astype(np.float64) - md).max()
+            assert merr <= MASS_ATOL, f"{name} mass b{b}h{h} err {merr:.3e}"
+
+    for tau in TAUS:
+        _say(f"[parity] {name}: select tau={tau}")
+        idx, count = losa.select(mass, tau)
+        _say(f"[parity] {name}: sparse tau={tau}")
+        os_, lses = losa.sparse_attn(tq, tk, tv, idx, count, block=blk, want_lse=True)
+        torch.cuda.synchronize()
+        idx_g, cnt_g, os_g, lses_g = _np(idx), _np(count), _np(os_), _np(lses)
+        for b in range(cfg.batch):
+            for h in range(cfg.heads):
+                ridx, rcnt = oracle.select(mass_g[b, h], tau)
+                assert np.array_equal(cnt_g[b, h], rcnt), f"{name} counts tau={tau} b{b}h{h}"
+                for i in range(nb):
+                    c = rcnt[i]
+                    assert np.array_equal(idx_g[b, h, i, :c], ridx[i, :c]), \
+                        f"{name} idx tau={tau} b{b}h{h} row {i}"
+                ref_o, ref_lse = oracle.sparse_attention(q[b, h], k[b, h], v[b, h],
+                                                         idx_g[b, h], cnt_g[b, h], blk)
+                _compare_attention(os_g[b, h], lses_g[b, h], ref_o, ref_lse,
+                                   f"{name} sparse tau={tau} b{b}h{h}")
+        if tau == 1.0:
+            # every block kept, visited in the same ascending order as the
+            # dense pass: the two kernels do identical arithmetic
+            assert (cnt_g == nb).all()
+            assert np.array_equal(os_g, o_g) and np.array_equal(lses_g, lse_g)
+
+
+def test_repeat_runs_are_bitwise_identical(losa):
+    cfg = CASES["N1280 D128 b64 many tiles"]
+    _say("[parity] determinism")
+    q, k, v = (_dev(x, cfg.dtype) for x in synth.make_inputs(cfg))
+    outs = []
+    for _ in range(2):
+        o, lse = losa.dense_attn(q, k, v, block=cfg.block)
+        m = losa.block_mass(q, k, block=cfg.block, lse=lse)
+        idx, cnt = losa.select(m, 0.99)
+        so, slse = losa.sparse_attn(q, k, v, idx, cnt, block=cfg.block, want_lse=True)
+        torch.cuda.synchronize()
+        outs.append([_np(t) for t in (o, lse, m, cnt, so, slse)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("d,blk,dtype", [(128, 64, "bf16"), (64, 128, "bf16"),
+                                         (64, 64, "fp32")])
+def test_sparse_arbitrary_lists(losa, d, blk, dtype):
+    """Lists in any order, single blocks, the short last block alone, an
+    empty list, and entries past count that must be ignored."""
+    cfg = synth.small_config(n_grid=(3, 7, 13), head_dim=d, block=blk, dtype=dtype,
+                             heads=2, alpha=(2.0, 0.5), seed=21)
+    _say(f"[parity] arbitrary lists d={d} block={blk} {dtype}")
+    q, k, v = synth.make_inputs(cfg)
+    nb = cfg.num_blocks
+    rng = np.random.default_rng(5)
+    idx = np.zeros((1, 2, nb, nb), np.int32)
+    cnt = np.zeros((1, 2, nb), np.int32)
+    for h in range(2):
+        for i in range(nb):
+            idx[0, h, i] = rng.permutation(nb)
+            cnt[0, h, i] = rng.integers(1, nb + 1)
+    idx[0, 0, 0, 0], cnt[0, 0, 0] = nb - 1, 1          # the short last block alone
+    idx[0, 1, 1, :2], cnt[0, 1, 1] = [nb - 1, 0], 2
+    cnt[0, 1, nb - 1] = 0                               # empty list
+    tq, tk, tv = (_dev(x, dtype) for x in (q, k, v))
+    o, lse = losa.sparse_attn(tq, tk, tv, torch.from_numpy(idx).cuda(),
+                              torch.from_numpy(cnt).cuda(), block=blk, want_lse=True)
+    torch.cuda.synchronize()
+    o_g, lse_g = _np(o), _np(lse)
+    for h in range(2):
+        qbs = [i for i in range(nb) if cnt[0, h, i] > 0]
+        ref_o, ref_lse = oracle.sparse_attention(q[0, h], k[0, h], v[0, h], idx[0, h],
+                                                 cnt[0, h], blk, qblocks=qbs)
+        rows = np.concatenate([np.arange(i * blk, min(cfg.seq_len, (i + 1) * blk)) for i in qbs])
+        _compare_attention(o_g[0, h, rows], lse_g[0, h, rows], ref_o, ref_lse, f"lists h{h}")
+    lo = (nb - 1) * blk
+    assert (o_g[0, 1, lo:] == 0).all() and np.isneginf(lse_g[0, 1, lo:]).all()
+
+
+@pytest.mark.parametrize("nkb", [1, 3, 16, 64, 65, 200, 512, 929, 1024])
+def test_select_matches_oracle_on_given_masses(losa, nkb):
+    _say(f"[parity] select nkb={nkb}")
+    rng = np.random.default_rng(nkb)
+    rows = 37
+    mass = np.empty((rows, nkb), np.float32)
+    for r in range(rows):
+        kind = r % 4
+        if kind == 0:
+            x = rng.dirichlet(np.full(nkb, 0.05))
+        elif kind == 1:
+            x = rng.dirichlet(np.full(nkb, 5.0))
+        elif kind == 2:
+            x = np.full(nkb, 1.0 / nkb)          # ties everywhere
+        else:
+            x = rng.dirichlet(np.full(nkb, 0.5))
+            x[rng.integers(0, nkb, max(1, nkb // 4))] = 0.0   # exact zeros
+        mass[r] = x.astype(np.float32)
+    tm = torch.from_numpy(mass).cuda()
+    for tau in TAUS + (0.3, 2.0):
+        idx, cnt = losa.select(tm, tau)
+        torch.cuda.synchronize()
+        idx_g, cnt_g = _np(idx), _np(cnt)
+        ridx, rcnt = oracle.select(mass, tau)
+        assert np.array_equal(cnt_g, rcnt), f"counts nkb={nkb} tau={tau}"
+        for r in range(rows):
+            assert np.array_equal(idx_g[r, :rcnt[r]], ridx[r, :rcnt[r]]), (nkb, tau, r)
+
+
+def test_select_golden_cases(losa, golden_dir):
+    import json
+    import os
+    cases = json.load(open(os.path.join(golden_dir, "select_worked.json")))["cases"]
+    for case in cases:
+        m = torch.tensor([case["masses"]], dtype=torch.float32).cuda()
+        idx, cnt = losa.select(m, case["tau"])
+        torch.cuda.synchronize()
+        assert int(cnt[0]) == case["count"], case["name"]
+        assert idx[0, :case["count"]].cpu().tolist() == case["idx"], case["name"]
+
+
+def test_scale_argument(losa):
+    cfg = synth.small_config(n_grid=(2, 5, 13), head_dim=64, block=64, alpha=(2.0, 1.0))
+    q, k, v = synth.make_inputs(cfg)
+    tq, tk, tv = (_dev(x, "bf16") for x in (q, k, v))
+    o, lse = losa.dense_attn(tq, tk, tv, block=64, scale=0.05)
+    torch.cuda.synchronize()
+    for h in range(2):
+        od, lsed = oracle.dense_attention(q[0, h], k[0, h], v[0, h], scale=0.05)
+        _compare_attention(_np(o)[0, h], _np(lse)[0, h], od, lsed, f"scale h{h}")
+    assert math.isfinite(float(lse.float().abs().max()))
