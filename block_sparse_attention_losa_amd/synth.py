@@ -107,20 +107,20 @@ def round_bf16(x) -> np.ndarray:
 
     Works on the binary64 encoding: the 52-bit fraction is rounded to bf16's
     7 bits (carries into the exponent are the usual round-up).  Only values
-    inside bf16's normal range (or zero) are accepted.
+    inside bf16's normal range (or zero) are accepted.  The integer
+    arithmetic runs on torch's multithreaded CPU kernels.
     """
-    x = np.ascontiguousarray(x, dtype=np.float64)
-    bits = x.view(np.uint64)
-    drop = np.uint64(45)
-    lsb = (bits >> drop) & np.uint64(1)
-    half_minus_one = np.uint64((1 << 44) - 1)
-    mask = np.uint64(~((1 << 45) - 1) & 0xFFFFFFFFFFFFFFFF)
-    out = ((bits + half_minus_one + lsb) & mask).view(np.float64)
-    mag = np.abs(out)
-    bad = (mag != 0) & ((mag < 2.0 ** -126) | ~np.isfinite(mag) | (mag >= 2.0 ** 128))
-    if bad.any():
+    import torch
+
+    bits = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64)).view(torch.int64)
+    out = ((bits >> 45) & 1) + ((1 << 44) - 1)
+    out += bits
+    out &= -(1 << 45)
+    res = out.view(torch.float64)
+    mag = res.abs()
+    if not bool((mag < 2.0 ** 128).all()) or bool(((mag < 2.0 ** -126) & (mag != 0)).any()):
         raise ValueError("value outside bf16's normal range")
-    return out
+    return res.numpy()
 
 
 def round_dtype(x, dtype: str) -> np.ndarray:
