@@ -28,7 +28,8 @@ METRIC = "sparse-attn ms/call + MFMA util at Wan2.1-1.3B shape (99% mass); x vs 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_wan13_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_attention_losa_amd", "csrc", "attn_fwd.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_attention_losa_amd", "csrc", f)
+                  for f in ("attn_bf16.hip", "losa_device.h")]
 
 
 def log(msg):
@@ -36,8 +37,13 @@ def log(msg):
 
 
 def kernel_hash():
-    with open(KERNEL_SOURCE, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    """Hash of the sources of the timed kernel (identifies the build a
+    counter summary was taken on)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def kept_flops(count, idx, n, block, d):

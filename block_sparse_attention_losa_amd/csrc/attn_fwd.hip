@@ -120,7 +120,8 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
   constexpr bool BF = G::kBf16;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  const int item = blockIdx.x;
+  const int item = xcd_item(blockIdx.x);
+  if (item >= p.items) return;  // padding of the XCD-aware grid
   const int nb = p.nb, N = p.n;
   const int bh = item / nb;
   const int qb = item - bh * nb;
@@ -168,19 +169,22 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
   constexpr int kQRegs = BF ? D / 16 : D / 2;
   using QElem = typename std::conditional<BF, bf16x8, float>::type;
   QElem qreg[kQRegs];
-  if constexpr (BF) {
+  constexpr int kRowBytes = D * (int)sizeof(T);
+  {
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qh, N * kRowBytes);
+    if constexpr (BF) {
 #pragma unroll
-    for (int dk = 0; dk < D / 16; ++dk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row_ok) x = *(const u32x4*)(qh + (size_t)row * D + dk * 16 + g * 8);
-      qreg[dk] = __builtin_bit_cast(bf16x8, x);
-    }
-  } else {
+      for (int dk = 0; dk < D / 16; ++dk)
+        qreg[dk] = __builtin_bit_cast(bf16x8, buf_load16(qr, row * kRowBytes + dk * 32 + g * 16));
+    } else {
 #pragma unroll
-    for (int s = 0; s < D / 2; s += 4) {
-      float4 x = {0.f, 0.f, 0.f, 0.f};
-      if (row_ok) x = *(const float4*)(qh + (size_t)row * D + g * (D / 2) + s);
-      qreg[s] = x.x; qreg[s + 1] = x.y; qreg[s + 2] = x.z; qreg[s + 3] = x.w;
+      for (int s = 0; s < D / 2; s += 4) {
+        const u32x4 x = buf_load16(qr, row * kRowBytes + (g * (D / 2) + s) * 4);
+        qreg[s] = __uint_as_float(x[0]);
+        qreg[s + 1] = __uint_as_float(x[1]);
+        qreg[s + 2] = __uint_as_float(x[2]);
+        qreg[s + 3] = __uint_as_float(x[3]);
+      }
     }
   }
 
@@ -189,45 +193,40 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
   u32x4 vr[BF ? 4 : G::kVChunksF];
   const bool v_thread = BF ? (tid < 2 * D) : true;  // bf16 V^T: 2*D blocks of 4 keys x 8 dims
 
-  auto load_stage = [&](int key0) {
+  // per-lane byte offsets inside a tile; the tile itself is addressed by a
+  // scalar buffer resource starting at its first key
+  const int v_kgrp = tid & 15, v_dgrp = tid >> 4;
+  auto load_k = [&](int key0) {
+    const int bytes = (N - key0) * kRowBytes;
+    const __amdgpu_buffer_rsrc_t kt =
+        make_rsrc((const unsigned char*)kh + (size_t)key0 * kRowBytes, bytes);
 #pragma unroll
-    for (int j = 0; j < G::kKChunks; ++j) {
-      const int c = j * 256 + tid;
-      const int key = c / (D * (int)sizeof(T) / 16);
-      const int col = c % (D * (int)sizeof(T) / 16);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key0 + key < N)
-        x = *(const u32x4*)((const unsigned char*)(kh + (size_t)(key0 + key) * D) + col * 16);
-      kr[j] = x;
-    }
+    for (int j = 0; j < G::kKChunks; ++j) kr[j] = buf_load16(kt, (j * 256 + tid) * 16);
+  };
+  auto load_v = [&](int key0) {
     if constexpr (G::kWithV) {
+      const int bytes = (N - key0) * kRowBytes;
+      const __amdgpu_buffer_rsrc_t vt =
+          make_rsrc((const unsigned char*)vh + (size_t)key0 * kRowBytes, bytes);
       if constexpr (BF) {
         if (v_thread) {
-          const int kgrp = tid & 15, dgrp = tid >> 4;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int key = kgrp * 4 + jj;
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (key0 + key < N) x = *(const u32x4*)(vh + (size_t)(key0 + key) * D + dgrp * 8);
-            vr[jj] = x;
-          }
+          for (int jj = 0; jj < 4; ++jj)
+            vr[jj] = buf_load16(vt, (v_kgrp * 4 + jj) * kRowBytes + v_dgrp * 16);
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < G::kVChunksF; ++j) {
-          const int c = j * 256 + tid;
-          const int key = c / (D / 4), col = c % (D / 4);
-          u32x4 x = {0u, 0u, 0u, 0u};
-          if (key0 + key < N) x = *(const u32x4*)(vh + (size_t)(key0 + key) * D + col * 4);
-          vr[j] = x;
-        }
+        for (int j = 0; j < G::kVChunksF; ++j) vr[j] = buf_load16(vt, (j * 256 + tid) * 16);
       }
     }
   };
 
-  auto store_stage = [&](int buf) {
-    unsigned char* base = smem + buf * G::kStage;
-    T* klds = (T*)base;
+  // LDS: two K tiles, then two V tiles (bf16: V^T)
+  auto kbuf = [&](int b) -> T* { return (T*)(smem + b * G::kKBytes); };
+  auto vbuf = [&](int b) -> T* { return (T*)(smem + 2 * G::kKBytes + b * G::kVBytes); };
+
+  auto store_k = [&](int b) {
+    T* klds = kbuf(b);
 #pragma unroll
     for (int j = 0; j < G::kKChunks; ++j) {
       const int c = j * 256 + tid;
@@ -235,11 +234,12 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
       const int col = c % (D * (int)sizeof(T) / 16);
       *(u32x4*)((unsigned char*)(klds + key * G::kKStr) + col * 16) = kr[j];
     }
+  };
+  auto store_v = [&](int b) {
     if constexpr (G::kWithV) {
-      T* vlds = (T*)(base + G::kKBytes);
+      T* vlds = vbuf(b);
       if constexpr (BF) {
         if (v_thread) {
-          const int kgrp = tid & 15, dgrp = tid >> 4;
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int w = i >> 1;
@@ -252,7 +252,7 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
               y = (vr[2][w] >> 16) | (vr[3][w] & 0xFFFF0000u);
             }
             u32x2 xy = {x, y};
-            *(u32x2*)(vlds + (dgrp * 8 + i) * G::kVStr + kgrp * 4) = xy;
+            *(u32x2*)(vlds + (v_dgrp * 8 + i) * G::kVStr + v_kgrp * 4) = xy;
           }
         }
       } else {
@@ -267,7 +267,7 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
   };
 
   auto key0_of = [&](int s) -> int {
-    const int blk = block_at(G::kSubs == 1 ? s : (s >> 1));
+    const int blk = __builtin_amdgcn_readfirstlane(block_at(G::kSubs == 1 ? s : (s >> 1)));
     return blk * BQ + (G::kSubs == 1 ? 0 : (s & 1) * 64);
   };
 
@@ -284,22 +284,9 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
   float lse_row = 0.f;      // kMass: the row's log-sum-exp (natural), +inf for padding rows
   if constexpr (MODE == kMass) lse_row = row_ok ? p.lse_in[(size_t)bh * N + row] : INFINITY;
 
-  if (nstage > 0) load_stage(key0_of(0));
-
-  for (int s = 0; s < nstage; ++s) {
-    const int buf = s & 1;
-    const int key0 = key0_of(s);
-    store_stage(buf);
-    __syncthreads();
-    if (s + 1 < nstage) load_stage(key0_of(s + 1));
-
-    const unsigned char* base = smem + buf * G::kStage;
-    const T* klds = (const T*)base;
-    const T* vlds = (const T*)(base + G::kKBytes);
-    const bool partial = key0 + 64 > N;
-
-    // ---- scores for this wave's chunks
-    f32x16 sc[G::kCPW];
+  // S^T of this wave's chunks of the K tile in buffer b
+  auto compute_s = [&](int b, f32x16 (&sc)[G::kCPW]) {
+    const T* klds = kbuf(b);
 #pragma unroll
     for (int cc = 0; cc < G::kCPW; ++cc) {
       const int chunk = G::kKS == 2 ? ks : cc;
@@ -322,13 +309,24 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
           sc[cc] = mfma_f32(a.w, qreg[st + 3], sc[cc]);
         }
       }
-      if (partial) {
+    }
+  };
+
+  // One pipelined step: the scores of tile t+1 are computed (MFMA) while
+  // tile t's scores go through the softmax (VALU); then tile t's P V
+  // product; then the next tiles are staged.  K runs one tile ahead of V.
+  auto step = [&](int t, f32x16 (&sc)[G::kCPW], f32x16 (&sn)[G::kCPW]) {
+    const int key0 = key0_of(t);
+    if (t + 1 < nstage) compute_s((t + 1) & 1, sn);
+    if (key0 + 64 > N) {
+#pragma unroll
+      for (int cc = 0; cc < G::kCPW; ++cc) {
+        const int chunk = G::kKS == 2 ? ks : cc;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (key0 + chunk * 32 + key_of_reg<BF>(i, g) >= N) sc[cc][i] = -INFINITY;
       }
     }
-
     if constexpr (MODE == kMass) {
       // exp(s - lse) summed over this wave's rows and keys of the tile
       float acc = 0.f;
@@ -340,7 +338,8 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
       acc = wave_sum(acc);
       if (lane == 0) part[wave * G::kMaxBlocks + (key0 / BQ)] += acc;
     } else {
-      // ---- online softmax with a lazily raised reference max
+      // online softmax with a lazily raised reference max: the reference
+      // moves only when a probability could exceed 2^8
       float mx = -INFINITY;
 #pragma unroll
       for (int cc = 0; cc < G::kCPW; ++cc)
@@ -348,32 +347,30 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[cc][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_cand = mx * c2;
-      // raise the reference only when a probability could exceed 2^8
       const bool raise = m_cand > m_run + 8.0f;
-      if (__ballot(raise)) {
-        const float m_new = raise ? m_cand : m_run;
-        // 0 when m_run = -inf; lanes that keep their reference scale by 1
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-        l_run *= alpha;
-        if constexpr (G::kWithV) {
-#pragma unroll
-          for (int mt = 0; mt < kORegs; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[mt][i] *= alpha;
-        }
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      const float m_new = raise ? m_cand : m_run;
+      // 0 when m_run = -inf; lanes that keep their reference scale by 1
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       float pr[G::kCPW][16];
+      float lsum = 0.f;
 #pragma unroll
       for (int cc = 0; cc < G::kCPW; ++cc)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           pr[cc][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][i], c2, -m_use));
-          l_run += pr[cc][i];
+          lsum += pr[cc][i];
         }
-
+      l_run = __builtin_fmaf(l_run, alpha, lsum);
+      m_run = m_new;
       if constexpr (G::kWithV) {
+        if (__ballot(raise)) {
+#pragma unroll
+          for (int mt = 0; mt < kORegs; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[mt][i] *= alpha;
+        }
+        const T* vlds = vbuf(t & 1);
 #pragma unroll
         for (int cc = 0; cc < G::kCPW; ++cc) {
           const int chunk = G::kKS == 2 ? ks : cc;
@@ -406,6 +403,33 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
         }
       }
     }
+    // stage V(t+1) and K(t+2), then start loading V(t+2) and K(t+3)
+    if (t + 1 < nstage) store_v((t + 1) & 1);
+    if (t + 2 < nstage) store_k(t & 1);
+    if (t + 2 < nstage) load_v(key0_of(t + 2));
+    if (t + 3 < nstage) load_k(key0_of(t + 3));
+    __syncthreads();
+  };
+
+  f32x16 sa[G::kCPW], sb[G::kCPW];
+  if (nstage > 0) {
+    load_k(key0_of(0));
+    load_v(key0_of(0));
+    store_k(0);
+    store_v(0);
+    if (nstage > 1) load_k(key0_of(1));
+    __syncthreads();
+    compute_s(0, sa);
+    if (nstage > 1) {
+      store_k(1);
+      load_v(key0_of(1));
+    }
+    if (nstage > 2) load_k(key0_of(2));
+    __syncthreads();
+  }
+  for (int t = 0; t < nstage; t += 2) {
+    step(t, sa, sb);
+    if (t + 1 < nstage) step(t + 1, sb, sa);
   }
 
   // ------------------------------------------------------------ epilogue
@@ -490,7 +514,7 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                G::kLdsBytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(p.items), dim3(256), G::kLdsBytes, stream, p);
+  hipLaunchKernelGGL(kern, dim3(xcd_grid(p.items)), dim3(256), G::kLdsBytes, stream, p);
   return hipGetLastError();
 }
 
@@ -517,7 +541,7 @@ static hipError_t launch_dtype(int mode, int head_dim, int block, const AttnPara
 
 hipError_t launch_attn(int mode, int dtype, int head_dim, int block, const AttnParams& p,
                        hipStream_t stream) {
-  if (dtype == 0) return launch_dtype<bf16>(mode, head_dim, block, p, stream);
+  if (dtype == 0) return launch_attn_bf16(mode, head_dim, block, p, stream);
   if (dtype == 1) return launch_dtype<float>(mode, head_dim, block, p, stream);
   return hipErrorInvalidValue;
 }

@@ -45,11 +45,37 @@ __device__ __forceinline__ int wave_min(int x) {
   return x;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  bf16 a = (bf16)lo, b = (bf16)hi;
-  unsigned short ua = __builtin_bit_cast(unsigned short, a);
-  unsigned short ub = __builtin_bit_cast(unsigned short, b);
-  return (unsigned)ua | ((unsigned)ub << 16);
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2_t));
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zero, which is how the kernels read the ragged last block.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// Workgroup -> work item so that each XCD (workgroups are handed to the 8
+// XCDs round-robin) walks runs of kChunk consecutive items: neighbouring
+// query blocks, whose key-block lists overlap, then share one L2.
+constexpr int kXcds = 8;
+constexpr int kXcdChunk = 16;
+__host__ __device__ __forceinline__ int xcd_grid(int items) {
+  const int per = kXcds * kXcdChunk;
+  return (items + per - 1) / per * per;
+}
+__device__ __forceinline__ int xcd_item(int b) {
+  const int x = b % kXcds, k = b / kXcds;
+  return ((k / kXcdChunk) * kXcds + x) * kXcdChunk + (k % kXcdChunk);
 }
 
 }  // namespace losa

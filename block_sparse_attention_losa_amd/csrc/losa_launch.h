@@ -29,6 +29,10 @@ struct AttnParams {
 hipError_t launch_attn(int mode, int dtype, int head_dim, int block, const AttnParams& p,
                        hipStream_t stream);
 
+// bf16 kernels (LDS-DMA pipeline); same contract as launch_attn.
+hipError_t launch_attn_bf16(int mode, int head_dim, int block, const AttnParams& p,
+                            hipStream_t stream);
+
 hipError_t launch_select(int32_t rows, int32_t nkb, const float* mass, double tau,
                          int32_t* idx, int32_t* count, hipStream_t stream);
 
