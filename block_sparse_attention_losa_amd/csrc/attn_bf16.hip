@@ -6,13 +6,18 @@
 //   kMass   - second pass of the mass map: recompute the scores, take
 //             exp(s - lse) and sum each (query block, key block) tile.
 //
-// One workgroup (4 waves) owns one query block of BQ = block rows; each
-// wave owns 32 rows.  With 64-row blocks the two waves of a row group split
-// every 64-key tile in halves and merge their softmax states at the end.
+// One workgroup (4 waves) owns 128 query rows -- two 64-row query blocks or
+// one 128-row block -- and each wave owns 32 of them.  Every 64-key K/V
+// tile brought into LDS therefore feeds 128 rows, which halves the L2
+// traffic per flop compared with one 64-row block per workgroup; at 64 rows
+// the K/V feed alone would need the whole L2 bandwidth at MFMA peak.  For
+// sparse attention the workgroup walks the union of its query blocks' frozen
+// lists (ascending) and each wave skips the tiles its own block did not
+// keep.
 //
 // Data movement is CDNA4-native:
-//  * K and V tiles (64 keys) go from HBM straight into LDS with buffer loads
-//    in LDS mode (no VGPR staging, no LDS store instructions); rows past the
+//  * K and V tiles go from HBM straight into LDS with buffer loads in LDS
+//    mode (no VGPR staging, no LDS store instructions); rows past the
 //    sequence end read as zero through the buffer range check;
 //  * tiles are stored row-major with an XOR swizzle of their 16-byte chunks
 //    so that both the K fragment reads (ds_read_b128) and the transposing V
@@ -28,26 +33,26 @@
 // already sit in the B-operand layout of O^T += V^T P^T.  The K rows fed to
 // the A operand are permuted (bits 2 and 3 of the row swapped) so that each
 // lane's eight probabilities of a 16-key slice are consecutive keys.
+#include <type_traits>
+
 #include "losa_device.h"
 #include "losa_launch.h"
 
 namespace losa {
-namespace {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-template <int D, int BQ, int MODE>
+template <int D, int BLK, int MODE>
 struct GeoB {
   static constexpr bool kWithV = (MODE == kDense || MODE == kSparse);
-  static constexpr int kRG = BQ / 32;          // row groups of 32 rows
-  static constexpr int kKS = 4 / kRG;          // waves sharing a row group
-  static constexpr int kCPW = 2 / kKS;         // 32-key chunks per wave per tile
-  static constexpr int kSubs = BQ / 64;        // 64-key tiles per key block
+  static constexpr int kRows = 128;             // query rows per workgroup
+  static constexpr int kQPW = kRows / BLK;      // query blocks per workgroup
+  static constexpr int kWavesPerBlock = 4 / kQPW;
+  static constexpr int kSubs = BLK / 64;        // 64-key tiles per key block
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kTileBytes = 64 * kRowBytes;
   static constexpr int kChunksPerRow = kRowBytes / 16;
-  static constexpr int kRowsPer256 = 256 / kRowBytes;   // rows sharing one bank sweep
   static constexpr int kBlocksPerTile = kTileBytes / 1024;  // 1 KB per wave-wide load
   static constexpr int kBlocksPerWave = kBlocksPerTile / 4;
   static constexpr int kRowsPerBlock = 1024 / kRowBytes;
@@ -55,8 +60,6 @@ struct GeoB {
   static constexpr int kRingBytes = (kWithV ? 4 : 2) * kTileBytes;  // 2 K + 2 V tiles
   static constexpr int kAuxBytes =
       MODE == kSparse ? (2 * kMaxBlocks + 16) * 4 : (MODE == kMass ? 4 * kMaxBlocks * 4 : 0);
-  static constexpr int kCombineBytes = (kKS == 2) ? kRG * (2 + (kWithV ? D : 0)) * 32 * 4 : 0;
-  static_assert(kCombineBytes <= kRingBytes, "combine buffer must fit in the ring");
   static constexpr int kLdsBytes = kRingBytes + kAuxBytes;
 };
 
@@ -100,17 +103,28 @@ __device__ __forceinline__ v4i16 ds_read_tr16(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
 }
 
-__device__ int build_ascending_list_b(const int32_t* __restrict__ idx_row, int cnt, int nb,
-                                      int* flag, int* list, int* ccount) {
+// Union of the frozen lists of up to kQPW query blocks, ascending, written
+// to list[] as (block | member_bits << 16); returns its length.
+template <int kQPW>
+__device__ int build_union_list(const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
+                                size_t row0, int nrows, int nb, int* flag, int* list,
+                                int* ccount) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nchunks = (nb + 63) >> 6;
   for (int j = tid; j < nchunks * 64; j += 256) flag[j] = 0;
   __syncthreads();
-  for (int t = tid; t < cnt; t += 256) {
-    const int j = idx_row[t];
-    if ((unsigned)j < (unsigned)nb) flag[j] = 1;
+#pragma unroll
+  for (int q = 0; q < kQPW; ++q) {
+    if (q < nrows) {
+      const int c = min(max(cnt[row0 + q], 0), nb);  // never read past the row
+      const int32_t* row = idx + (row0 + q) * nb;
+      for (int t = tid; t < c; t += 256) {
+        const int j = row[t];
+        if ((unsigned)j < (unsigned)nb) flag[j] |= 1 << q;
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
   for (int c = wave; c < nchunks; c += 4) {
     const unsigned long long m = __ballot(flag[c * 64 + lane] != 0);
     if (lane == 0) ccount[c] = __popcll(m);
@@ -121,27 +135,29 @@ __device__ int build_ascending_list_b(const int32_t* __restrict__ idx_row, int c
   for (int c = wave; c < nchunks; c += 4) {
     int base = 0;
     for (int c2 = 0; c2 < c; ++c2) base += ccount[c2];
-    const bool f = flag[c * 64 + lane] != 0;
-    const unsigned long long m = __ballot(f);
-    if (f) {
+    const int f = flag[c * 64 + lane];
+    const unsigned long long m = __ballot(f != 0);
+    if (f != 0) {
       const unsigned long long below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
-      list[base + __popcll(below)] = c * 64 + lane;
+      list[base + __popcll(below)] = (c * 64 + lane) | (f << 16);
     }
   }
   __syncthreads();
   return total;
 }
 
-template <int D, int BQ, int MODE>
+template <int D, int BLK, int MODE>
 __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
-  using G = GeoB<D, BQ, MODE>;
+  using G = GeoB<D, BLK, MODE>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
-  const int item = xcd_item(blockIdx.x);
-  if (item >= p.items) return;  // padding of the XCD-aware grid
   const int nb = p.nb, N = p.n;
-  const int bh = item / nb;
-  const int qb = item - bh * nb;
+  const int bh_count = p.items / nb;
+  const int wph = (nb + G::kQPW - 1) / G::kQPW;  // workgroups per (batch, head)
+  const int item = xcd_item(blockIdx.x, wph, bh_count);
+  if (item < 0) return;  // padding of the XCD-aware grid
+  const int bh = item / wph;
+  const int w = item - bh * wph;
   const size_t head_off = (size_t)bh * (size_t)N * D;
   const bf16* __restrict__ qh = (const bf16*)p.q + head_off;
   const bf16* __restrict__ kh = (const bf16*)p.k + head_off;
@@ -149,20 +165,20 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
-  const int rg = wave % G::kRG, ks = wave / G::kRG;
-  const int row = qb * BQ + rg * 32 + l32;
+  const int qi = wave / G::kWavesPerBlock;  // this wave's query block within the workgroup
+  const int row = w * G::kRows + wave * 32 + l32;
   const bool row_ok = row < N;
 
-  // ---- key blocks visited, in ascending order
+  // ---- key blocks visited, in ascending order, with member bits
   int nblk = nb;
   const int* list = nullptr;
   if constexpr (MODE == kSparse) {
     int* flag = (int*)(smem + G::kRingBytes);
     int* lst = flag + G::kMaxBlocks;
     int* ccount = lst + G::kMaxBlocks;
-    const size_t r = (size_t)bh * nb + qb;
-    const int cnt = min(max(p.cnt[r], 0), nb);  // never read past the row
-    nblk = build_ascending_list_b(p.idx + r * nb, cnt, nb, flag, lst, ccount);
+    const int qb0 = w * G::kQPW;
+    nblk = build_union_list<G::kQPW>(p.idx, p.cnt, (size_t)bh * nb + qb0,
+                                     min(G::kQPW, nb - qb0), nb, flag, lst, ccount);
     list = lst;
   }
   float* part = nullptr;  // kMass: per-wave partial tile sums [4][nb]
@@ -170,20 +186,21 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
     part = (float*)(smem + G::kRingBytes);
     for (int j = tid; j < 4 * G::kMaxBlocks; j += 256) part[j] = 0.f;
   }
-  auto block_at = [&](int t) -> int {
+  auto entry_at = [&](int t) -> int {
     if constexpr (MODE == kSparse) {
-      return list[t];
+      return __builtin_amdgcn_readfirstlane(list[G::kSubs == 1 ? t : (t >> 1)]);
     } else {
-      return t;
+      return (G::kSubs == 1 ? t : (t >> 1)) | (((1 << G::kQPW) - 1) << 16);
     }
   };
   int ntile = nblk * G::kSubs;
-  if (G::kSubs == 2 && nblk > 0 && block_at(nblk - 1) == nb - 1 && (nb - 1) * BQ + 64 >= N)
+  if (G::kSubs == 2 && nblk > 0 && (entry_at(ntile - 1) & 0xFFFF) == nb - 1 &&
+      (nb - 1) * BLK + 64 >= N)
     --ntile;  // empty second half of a short last block
   auto key0_of = [&](int t) -> int {
-    const int blk = __builtin_amdgcn_readfirstlane(block_at(G::kSubs == 1 ? t : (t >> 1)));
-    return blk * BQ + (G::kSubs == 1 ? 0 : (t & 1) * 64);
+    return (entry_at(t) & 0xFFFF) * BLK + (G::kSubs == 1 ? 0 : (t & 1) * 64);
   };
+  auto member = [&](int t) -> bool { return ((entry_at(t) >> (16 + qi)) & 1) != 0; };
 
   // ---- Q^T as the B operand, in registers
   bf16x8 qreg[D / 16];
@@ -213,7 +230,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
         make_rsrc((const unsigned char*)src + (size_t)key0 * G::kRowBytes,
                   (N - key0) * G::kRowBytes);
     // wave-uniform LDS destination (M0 must come from a scalar register)
-    const unsigned base = __builtin_amdgcn_readfirstlane(lds_addr_of(slot) + wave * G::kBlocksPerWave * 1024);
+    const unsigned base =
+        __builtin_amdgcn_readfirstlane(lds_addr_of(slot) + wave * G::kBlocksPerWave * 1024);
 #pragma unroll
     for (int j = 0; j < G::kBlocksPerWave; ++j) dma16(rs, base + j * 1024, off[j]);
   };
@@ -231,13 +249,12 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
   float lse_row = 0.f;      // kMass: the row's lse (natural), +inf on padding rows
   if constexpr (MODE == kMass) lse_row = row_ok ? p.lse_in[(size_t)bh * N + row] : INFINITY;
 
-  // S^T of this wave's chunks of the K tile in `slot`
+  // S^T of this wave's 32 rows against both 32-key chunks of the K tile
   const int prow = perm_row(l32);
-  auto compute_s = [&](const unsigned char* slot, f32x16 (&sc)[G::kCPW]) {
+  auto compute_s = [&](const unsigned char* slot, f32x16 (&sc)[2]) {
 #pragma unroll
-    for (int cc = 0; cc < G::kCPW; ++cc) {
-      const int chunk = G::kKS == 2 ? ks : cc;
-      const int r = chunk * 32 + prow;
+    for (int cc = 0; cc < 2; ++cc) {
+      const int r = cc * 32 + prow;
       const unsigned char* krow = slot + r * G::kRowBytes;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[cc][i] = 0.f;
@@ -263,42 +280,34 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
     const v4i16 lo = ds_read_tr16(slot + r0 * G::kRowBytes + swz_v<D>(r0, c) * 16 + sub);
     const v4i16 hi = ds_read_tr16(slot + r1 * G::kRowBytes + swz_v<D>(r1, c) * 16 + sub);
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-    const u32x4 w = {l2[0], l2[1], h2[0], h2[1]};
-    return __builtin_bit_cast(bf16x8, w);
+    const u32x4 wv = {l2[0], l2[1], h2[0], h2[1]};
+    return __builtin_bit_cast(bf16x8, wv);
   };
 
-  auto step = [&](int t, f32x16 (&sc)[G::kCPW], f32x16 (&sn)[G::kCPW]) {
-    const int key0 = key0_of(t);
-    // loads for later tiles: K(t+2) into the K slot freed by tile t, V(t+1)
-    // into the V slot freed by tile t-1
-    if (t + 2 < ntile) dma_tile(kh, key0_of(t + 2), kslot[t & 1], koff);
-    if constexpr (G::kWithV)
-      if (t + 1 < ntile) dma_tile(vh, key0_of(t + 1), vslot[(t + 1) & 1], voff);
-    if (t + 1 < ntile) compute_s(kslot[(t + 1) & 1], sn);
-    if (key0 + 64 > N) {
+  // softmax of tile t (scores in sc) and its P V product
+  auto consume = [&](int t, int key0, f32x16 (&sc)[2], auto masked) {
+    if constexpr (decltype(masked)::value) {
 #pragma unroll
-      for (int cc = 0; cc < G::kCPW; ++cc) {
-        const int chunk = G::kKS == 2 ? ks : cc;
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (key0 + chunk * 32 + perm_row(c_row(i, g)) >= N) sc[cc][i] = -INFINITY;
-      }
+          if (key0 + cc * 32 + perm_row(c_row(i, g)) >= N) sc[cc][i] = -INFINITY;
     }
     if constexpr (MODE == kMass) {
       float acc = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < G::kCPW; ++cc)
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][i], p.scale, -lse_row) * kLog2e);
       acc = wave_sum(acc);
-      if (lane == 0) part[wave * G::kMaxBlocks + (key0 / BQ)] += acc;
+      if (lane == 0) part[wave * G::kMaxBlocks + (key0 / BLK)] += acc;
     } else {
       // online softmax; the reference max is raised only when a probability
       // could exceed 2^8
       float mx = -INFINITY;
 #pragma unroll
-      for (int cc = 0; cc < G::kCPW; ++cc)
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[cc][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -307,10 +316,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
       const float m_new = raise ? m_cand : m_run;
       const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      float pr[G::kCPW][16];
+      float pr[2][16];
       float lsum = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < G::kCPW; ++cc)
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           pr[cc][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][i], c2, -m_use));
@@ -327,8 +336,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
         }
         const unsigned char* vs = vslot[t & 1];
 #pragma unroll
-        for (int cc = 0; cc < G::kCPW; ++cc) {
-          const int chunk = G::kKS == 2 ? ks : cc;
+        for (int cc = 0; cc < 2; ++cc) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             u32x4 pk;
@@ -339,83 +347,106 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
 #pragma unroll
             for (int mt = 0; mt < kORegs; ++mt) {
-              const bf16x8 a = v_operand(vs, chunk * 32 + h * 16 + g * 8, mt);
+              const bf16x8 a = v_operand(vs, cc * 32 + h * 16 + g * 8, mt);
               oacc[mt] = mfma_bf16(a, pb, oacc[mt]);
             }
           }
         }
       }
     }
+  };
+
+  // One pipelined step.  `masked` is true only for a final tile that runs
+  // past the sequence end (ascending lists put the short last block last).
+  auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2], auto masked) {
+    const int key0 = key0_of(t);
+    // loads for later tiles: K(t+2) into the K slot freed by tile t, V(t+1)
+    // into the V slot freed by tile t-1
+    if (t + 2 < ntile) dma_tile(kh, key0_of(t + 2), kslot[t & 1], koff);
+    if constexpr (G::kWithV)
+      if (t + 1 < ntile) dma_tile(vh, key0_of(t + 1), vslot[(t + 1) & 1], voff);
+    if constexpr (MODE == kSparse) {
+      // waves skip the tiles their query block did not keep
+      if (t + 1 < ntile && member(t + 1)) compute_s(kslot[(t + 1) & 1], sn);
+      if (member(t)) consume(t, key0, sc, masked);
+    } else {
+      // scores of the next tile; after the last tile this reads a stale
+      // slot and the result is dropped, which keeps the block branch-free
+      compute_s(kslot[(t + 1) & 1], sn);
+      consume(t, key0, sc, masked);
+    }
     wait_dma_all();
     __syncthreads();
   };
 
-  f32x16 sa[G::kCPW], sb[G::kCPW];
+  using Plain = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  f32x16 sa[2], sb[2];
   if (ntile > 0) {
     dma_tile(kh, key0_of(0), kslot[0], koff);
     if constexpr (G::kWithV) dma_tile(vh, key0_of(0), vslot[0], voff);
     if (ntile > 1) dma_tile(kh, key0_of(1), kslot[1], koff);
+  }
+  // Consume Q (and the row lse) here, on every path: the compiler then waits
+  // for those loads once, before the loop, instead of placing vmcnt waits
+  // inside the loop where they would also stall on the tile loads in flight.
+#pragma unroll
+  for (int dk = 0; dk < D / 16; ++dk) asm volatile("" ::"v"(qreg[dk]));
+  asm volatile("" ::"v"(lse_row));
+  if (ntile > 0) {
     wait_dma_all();
     __syncthreads();
-    compute_s(kslot[0], sa);
+    if (MODE != kSparse || member(0)) compute_s(kslot[0], sa);
     __syncthreads();  // K slot 0 may be refilled from here on
   }
-  for (int t = 0; t < ntile; t += 2) {
-    step(t, sa, sb);
-    if (t + 1 < ntile) step(t + 1, sb, sa);
+  const bool last_short = ntile > 0 && key0_of(ntile - 1) + 64 > N;
+  const int nplain = ntile - (last_short ? 1 : 0);
+  int t = 0;
+  for (; t + 1 < nplain; t += 2) {
+    step(t, sa, sb, Plain());
+    step(t + 1, sb, sa, Plain());
+  }
+  if (t < nplain) {
+    step(t, sa, sb, Plain());
+    ++t;
+  }
+  if (last_short) {
+    if (t & 1)
+      step(t, sb, sa, Masked());
+    else
+      step(t, sa, sb, Masked());
   }
 
   // ------------------------------------------------------------ epilogue
   if constexpr (MODE == kMass) {
     __syncthreads();
-    const float inv_rows = 1.0f / (float)min(BQ, N - qb * BQ);
-    float* out = p.mass + ((size_t)bh * nb + qb) * nb;
-    for (int j = tid; j < nb; j += 256) {
-      const float t = (part[j] + part[G::kMaxBlocks + j]) +
-                      (part[2 * G::kMaxBlocks + j] + part[3 * G::kMaxBlocks + j]);
-      out[j] = t * inv_rows;
+#pragma unroll
+    for (int q = 0; q < G::kQPW; ++q) {
+      const int qb = w * G::kQPW + q;
+      if (qb < nb) {
+        const float inv_rows = 1.0f / (float)min(BLK, N - qb * BLK);
+        float* out = p.mass + ((size_t)bh * nb + qb) * nb;
+        const float* pw = part + q * G::kWavesPerBlock * G::kMaxBlocks;
+        for (int j = tid; j < nb; j += 256) {
+          float tot;
+          if constexpr (G::kWavesPerBlock == 4) {
+            tot = (pw[j] + pw[G::kMaxBlocks + j]) +
+                  (pw[2 * G::kMaxBlocks + j] + pw[3 * G::kMaxBlocks + j]);
+          } else {
+            tot = pw[j] + pw[G::kMaxBlocks + j];
+          }
+          out[j] = tot * inv_rows;
+        }
+      }
     }
     return;
   } else {
-    float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    float m_fin = m_run;
-    if constexpr (G::kKS == 2) {
-      // merge the two key halves of each row group through LDS
-      __syncthreads();
-      float* cb = (float*)smem + rg * (2 + (G::kWithV ? D : 0)) * 32;
-      if (ks == 1) {
-        if (g == 0) {
-          cb[l32] = m_run;
-          cb[32 + l32] = l_tot;
-        }
-        if constexpr (G::kWithV) {
-#pragma unroll
-          for (int mt = 0; mt < kORegs; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) cb[64 + (mt * 32 + c_row(i, g)) * 32 + l32] = oacc[mt][i];
-        }
-      }
-      __syncthreads();
-      if (ks == 1) return;
-      const float m1 = cb[l32], l1 = cb[32 + l32];
-      const float mm = fmaxf(m_run, m1);
-      const float a0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
-      const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
-      l_tot = a0 * l_tot + a1 * l1;
-      m_fin = mm;
-      if constexpr (G::kWithV) {
-#pragma unroll
-        for (int mt = 0; mt < kORegs; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            oacc[mt][i] = a0 * oacc[mt][i] + a1 * cb[64 + (mt * 32 + c_row(i, g)) * 32 + l32];
-      }
-    }
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (!row_ok) return;
     const bool empty = !(l_tot > 0.f);
     if (p.lse != nullptr && g == 0) {
       p.lse[(size_t)bh * N + row] =
-          empty ? -INFINITY : (m_fin + __builtin_amdgcn_logf(l_tot)) * kLn2;
+          empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
     if constexpr (G::kWithV) {
       const float inv = empty ? 0.f : 1.0f / l_tot;
@@ -425,38 +456,38 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int d0 = mt * 32 + 8 * i4 + 4 * g;
-          u32x2 w = {pack_bf16x2(oacc[mt][4 * i4 + 0] * inv, oacc[mt][4 * i4 + 1] * inv),
-                     pack_bf16x2(oacc[mt][4 * i4 + 2] * inv, oacc[mt][4 * i4 + 3] * inv)};
-          *(u32x2*)(orow + d0) = w;
+          u32x2 wv = {pack_bf16x2(oacc[mt][4 * i4 + 0] * inv, oacc[mt][4 * i4 + 1] * inv),
+                      pack_bf16x2(oacc[mt][4 * i4 + 2] * inv, oacc[mt][4 * i4 + 3] * inv)};
+          *(u32x2*)(orow + d0) = wv;
         }
     }
   }
 }
 
-template <int D, int BQ, int MODE>
+template <int D, int BLK, int MODE>
 hipError_t launch_b(const AttnParams& p, hipStream_t stream) {
-  using G = GeoB<D, BQ, MODE>;
-  auto kern = attn_bf16_kernel<D, BQ, MODE>;
+  using G = GeoB<D, BLK, MODE>;
+  auto kern = attn_bf16_kernel<D, BLK, MODE>;
   static hipError_t attr = hipFuncSetAttribute((const void*)kern,
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                G::kLdsBytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(xcd_grid(p.items)), dim3(256), G::kLdsBytes, stream, p);
+  const int wph = (p.nb + G::kQPW - 1) / G::kQPW;
+  hipLaunchKernelGGL(kern, dim3(xcd_grid(wph, p.items / p.nb)), dim3(256), G::kLdsBytes, stream,
+                     p);
   return hipGetLastError();
 }
 
-template <int D, int BQ>
+template <int D, int BLK>
 hipError_t launch_b_mode(int mode, const AttnParams& p, hipStream_t stream) {
   switch (mode) {
-    case kDense: return launch_b<D, BQ, kDense>(p, stream);
-    case kSparse: return launch_b<D, BQ, kSparse>(p, stream);
-    case kLse: return launch_b<D, BQ, kLse>(p, stream);
-    case kMass: return launch_b<D, BQ, kMass>(p, stream);
+    case kDense: return launch_b<D, BLK, kDense>(p, stream);
+    case kSparse: return launch_b<D, BLK, kSparse>(p, stream);
+    case kLse: return launch_b<D, BLK, kLse>(p, stream);
+    case kMass: return launch_b<D, BLK, kMass>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
-
-}  // namespace
 
 hipError_t launch_attn_bf16(int mode, int head_dim, int block, const AttnParams& p,
                             hipStream_t stream) {

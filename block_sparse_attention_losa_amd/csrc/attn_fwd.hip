@@ -120,8 +120,8 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
   constexpr bool BF = G::kBf16;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  const int item = xcd_item(blockIdx.x);
-  if (item >= p.items) return;  // padding of the XCD-aware grid
+  const int item = xcd_item(blockIdx.x, p.nb, p.items / p.nb);
+  if (item < 0) return;  // padding of the XCD-aware grid
   const int nb = p.nb, N = p.n;
   const int bh = item / nb;
   const int qb = item - bh * nb;
@@ -514,7 +514,7 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                G::kLdsBytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(xcd_grid(p.items)), dim3(256), G::kLdsBytes, stream, p);
+  hipLaunchKernelGGL(kern, dim3(xcd_grid(p.nb, p.items / p.nb)), dim3(256), G::kLdsBytes, stream, p);
   return hipGetLastError();
 }
 

@@ -64,18 +64,23 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
-// Workgroup -> work item so that each XCD (workgroups are handed to the 8
-// XCDs round-robin) walks runs of kChunk consecutive items: neighbouring
-// query blocks, whose key-block lists overlap, then share one L2.
+// Workgroup -> work item.  Workgroups are handed to the 8 XCDs round-robin
+// (workgroup b runs on XCD b % 8).  Each XCD is given the same contiguous
+// slice of query blocks -- [x*per, (x+1)*per) with per = ceil(nb/8) -- of
+// every (batch, head), heads in order: neighbouring query blocks, whose
+// key-block lists overlap, share one L2, every XCD sees the same mix of
+// cheap and expensive heads, and a head's K/V is live in all L2s at once.
 constexpr int kXcds = 8;
-constexpr int kXcdChunk = 16;
-__host__ __device__ __forceinline__ int xcd_grid(int items) {
-  const int per = kXcds * kXcdChunk;
-  return (items + per - 1) / per * per;
+__host__ __device__ __forceinline__ int xcd_slice(int nb) { return (nb + kXcds - 1) / kXcds; }
+__host__ __device__ __forceinline__ int xcd_grid(int nb, int bh_count) {
+  return kXcds * xcd_slice(nb) * bh_count;
 }
-__device__ __forceinline__ int xcd_item(int b) {
+// Returns the work item (bh * nb + qb) of workgroup b, or -1 for padding.
+__device__ __forceinline__ int xcd_item(int b, int nb, int bh_count) {
+  const int per = xcd_slice(nb);
   const int x = b % kXcds, k = b / kXcds;
-  return ((k / kXcdChunk) * kXcds + x) * kXcdChunk + (k % kXcdChunk);
+  const int bh = k / per, qb = x * per + (k - (k / per) * per);
+  return (bh < bh_count && qb < nb) ? bh * nb + qb : -1;
 }
 
 }  // namespace losa
