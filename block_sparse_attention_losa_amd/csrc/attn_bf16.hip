@@ -75,6 +75,10 @@ __device__ __forceinline__ int swz_v(int r, int c) {
   return c ^ (((r / rows256) & (groups - 1)) << 2);
 }
 
+// Online-softmax reference max: probabilities are exp2(s - m) with
+// s - m < kRaise; the reference moves (and O is rescaled) only past that.
+constexpr float kRaise = 16.0f;
+
 __device__ __forceinline__ int perm_row(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
@@ -304,7 +308,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
       if (lane == 0) part[wave * G::kMaxBlocks + (key0 / BLK)] += acc;
     } else {
       // online softmax; the reference max is raised only when a probability
-      // could exceed 2^8
+      // could exceed 2^kRaise, so O is rarely rescaled
       float mx = -INFINITY;
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
@@ -312,7 +316,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[cc][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_cand = mx * c2;
-      const bool raise = m_cand > m_run + 8.0f;
+      const bool raise = m_cand > m_run + kRaise;
       const float m_new = raise ? m_cand : m_run;
       const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -366,8 +370,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
     if constexpr (G::kWithV)
       if (t + 1 < ntile) dma_tile(vh, key0_of(t + 1), vslot[(t + 1) & 1], voff);
     if constexpr (MODE == kSparse) {
-      // waves skip the tiles their query block did not keep
-      if (t + 1 < ntile && member(t + 1)) compute_s(kslot[(t + 1) & 1], sn);
+      // waves skip the softmax and P V of tiles their query block did not
+      // keep; the next tile's scores are computed regardless (the union
+      // exceeds each list by ~3 %), which keeps that work branch-free
+      compute_s(kslot[(t + 1) & 1], sn);
       if (member(t)) consume(t, key0, sc, masked);
     } else {
       // scores of the next tile; after the last tile this reads a stale
