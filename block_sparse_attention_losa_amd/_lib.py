@@ -20,6 +20,7 @@ STATUS_NAMES = {
     5: "LOSA_ERR_MISALIGNED",
     6: "LOSA_ERR_DEVICE",
     7: "LOSA_ERR_BAD_ARGUMENT",
+    8: "LOSA_ERR_WORKSPACE",
 }
 LOSA_BF16 = 0
 LOSA_FP32 = 1
@@ -57,6 +58,9 @@ SIGNATURES = {
     "losa_num_blocks": (ctypes.c_int32, [_DESC]),
     "losa_dense_attn": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP, _VP, _VP]),
     "losa_block_mass": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "losa_dense_attn_mass_workspace": (ctypes.c_int64, [_DESC]),
+    "losa_dense_attn_mass": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                            ctypes.c_int64, _VP]),
     "losa_select": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_double,
                                    _VP, _VP, _VP]),
     "losa_sparse_attn": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),

@@ -83,6 +83,42 @@ def block_mass(q, k, block: int = 64, lse=None, scale=None, mass=None, lse_scrat
     return mass
 
 
+def dense_attn_mass_workspace_bytes(q, block: int = 64) -> int:
+    """Workspace bytes :func:`dense_attn_mass` needs for inputs shaped like q."""
+    n = _lib.load().losa_dense_attn_mass_workspace(make_desc(q, block))
+    if n < 0:
+        raise ValueError("unsupported shape for dense_attn_mass")
+    return int(n)
+
+
+def dense_attn_mass(q, k, v, block: int = 64, scale=None, o=None, lse=None, mass=None,
+                    workspace=None, want_lse=True):
+    """Construction step in one sweep: dense attention and the block mass map
+    of the same inputs.  Returns ``(o, lse, mass)``.  ``workspace`` is a
+    uint8 device tensor of at least :func:`dense_attn_mass_workspace_bytes`
+    bytes (allocated here when None)."""
+    _check_inputs(q, k, v)
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    desc = make_desc(q, block, scale)
+    b, h, n, _ = q.shape
+    nb = num_blocks(n, block)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    if mass is None:
+        mass = torch.empty((b, h, nb, nb), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(dense_attn_mass_workspace_bytes(q, block), dtype=torch.uint8,
+                                device=q.device)
+    lib = _lib.load()
+    _lib.check("losa_dense_attn_mass", lib.losa_dense_attn_mass(
+        desc, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(mass), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q)))
+    return o, lse, mass
+
+
 def select(mass, threshold: float = 0.99, idx=None, count=None):
     """Threshold selection over the last axis of ``mass``; returns
     ``(idx, count)`` with idx shaped like mass (int32; entries at and past

@@ -4,7 +4,12 @@
 //   kSparse - the same over the frozen key-block list of each query block;
 //   kLse    - the row log-sum-exp alone (first pass of the mass map);
 //   kMass   - second pass of the mass map: recompute the scores, take
-//             exp(s - lse) and sum each (query block, key block) tile.
+//             exp(s - lse) and sum each (query block, key block) tile;
+//   kDenseMass - kDense that also leaves, for every row i and key block J,
+//             log2 of the block's share of the row's softmax sum, taken
+//             against a per-row reference, in a workspace; once the row's
+//             lse is known a small fold turns these into the mass map, so
+//             the construction step needs one sweep over the keys, not two.
 //
 // One workgroup (4 waves) owns 128 query rows -- two 64-row query blocks or
 // one 128-row block -- and each wave owns 32 of them.  Every 64-key K/V
@@ -45,7 +50,7 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 template <int D, int BLK, int MODE>
 struct GeoB {
-  static constexpr bool kWithV = (MODE == kDense || MODE == kSparse);
+  static constexpr bool kWithV = (MODE == kDense || MODE == kSparse || MODE == kDenseMass);
   static constexpr int kRows = 128;             // query rows per workgroup
   static constexpr int kQPW = kRows / BLK;      // query blocks per workgroup
   static constexpr int kWavesPerBlock = 4 / kQPW;
@@ -251,6 +256,18 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
   float l_run = 0.f;        // this lane's partial row sum
   const float c2 = p.scale * kLog2e;
   float lse_row = 0.f;      // kMass: the row's lse (natural), +inf on padding rows
+  float tacc = 0.f;         // kDenseMass: current key block's share of the row sum
+  float m0 = 0.f;           // kDenseMass: reference of the first key block
+  float pend = 0.f;         // kDenseMass: finished block sum not yet stored ...
+  int pend_kb = -1;         // ... and its key block (-1: none)
+  auto flush_rowsum = [&]() {
+    if constexpr (MODE == kDenseMass) {
+      if (pend_kb >= 0) {
+        if (g == 0 && row_ok) p.rowsum[((size_t)bh * nb + pend_kb) * N + row] = pend;
+        pend_kb = -1;
+      }
+    }
+  };
   if constexpr (MODE == kMass) lse_row = row_ok ? p.lse_in[(size_t)bh * N + row] : INFINITY;
 
   // S^T of this wave's 32 rows against both 32-key chunks of the K tile
@@ -314,7 +331,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[cc][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = pair_max(mx);
       const float m_cand = mx * c2;
       const bool raise = m_cand > m_run + kRaise;
       const float m_new = raise ? m_cand : m_run;
@@ -331,6 +348,22 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
         }
       l_run = __builtin_fmaf(l_run, alpha, lsum);
       m_run = m_new;
+      if constexpr (MODE == kDenseMass) {
+        // the tile's part of the row sum (both lanes of the row), against
+        // the current reference and accumulated over the key block's tiles;
+        // after the block's last tile, log2 of it relative to m0 is stored
+        // -- at the start of the next step, ahead of that step's tile loads:
+        // stores count in vmcnt, and a store issued here would make the
+        // end-of-step wait for the loads also wait for its write-back
+        tacc = __builtin_fmaf(tacc, alpha, pair_sum(lsum));
+        if (G::kSubs == 1 || (key0 % BLK) == BLK - 64 || key0 + 64 >= N) {
+          const int kb = key0 / BLK;
+          if (kb == 0) m0 = m_run;
+          pend = (m_run - m0) + __builtin_amdgcn_logf(tacc);
+          pend_kb = kb;
+          tacc = 0.f;
+        }
+      }
       if constexpr (G::kWithV) {
         if (__ballot(raise)) {
 #pragma unroll
@@ -364,6 +397,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
   // past the sequence end (ascending lists put the short last block last).
   auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2], auto masked) {
     const int key0 = key0_of(t);
+    flush_rowsum();
     // loads for later tiles: K(t+2) into the K slot freed by tile t, V(t+1)
     // into the V slot freed by tile t-1
     if (t + 2 < ntile) dma_tile(kh, key0_of(t + 2), kslot[t & 1], koff);
@@ -457,12 +491,17 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
     }
     return;
   } else {
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    flush_rowsum();
+    const float l_tot = pair_sum(l_run);
     if (!row_ok) return;
     const bool empty = !(l_tot > 0.f);
     if (p.lse != nullptr && g == 0) {
       p.lse[(size_t)bh * N + row] =
           empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+    if constexpr (MODE == kDenseMass) {
+      // log2 of the row sum against m0: the fold divides by it
+      if (g == 0) p.rowref[(size_t)bh * N + row] = (m_run - m0) + __builtin_amdgcn_logf(l_tot);
     }
     if constexpr (G::kWithV) {
       const float inv = empty ? 0.f : 1.0f / l_tot;
@@ -501,6 +540,7 @@ hipError_t launch_b_mode(int mode, const AttnParams& p, hipStream_t stream) {
     case kSparse: return launch_b<D, BLK, kSparse>(p, stream);
     case kLse: return launch_b<D, BLK, kLse>(p, stream);
     case kMass: return launch_b<D, BLK, kMass>(p, stream);
+    case kDenseMass: return launch_b<D, BLK, kDenseMass>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

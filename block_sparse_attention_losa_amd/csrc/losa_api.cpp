@@ -42,6 +42,17 @@ losa::AttnParams base_params(const losa_attn_desc* d, int32_t nb) {
 
 losa_status device_status(hipError_t e) { return e == hipSuccess ? LOSA_OK : LOSA_ERR_DEVICE; }
 
+// Workspace of losa_dense_attn_mass: the per-row block sums [B*H, nb, N]
+// fp32, then the per-row offsets [B*H, N] fp32 at the next 256-byte
+// boundary.
+int64_t rowsum_bytes(const losa_attn_desc* d, int32_t nb) {
+  const int64_t raw = int64_t{4} * d->batch * d->heads * nb * d->seq_len;
+  return (raw + 255) / 256 * 256;
+}
+int64_t dense_mass_workspace(const losa_attn_desc* d, int32_t nb) {
+  return rowsum_bytes(d, nb) + int64_t{4} * d->batch * d->heads * d->seq_len;
+}
+
 }  // namespace
 
 extern "C" {
@@ -98,6 +109,57 @@ losa_status losa_block_mass(const losa_attn_desc* desc, const void* q, const voi
       losa::launch_attn(losa::kMass, desc->dtype, desc->head_dim, desc->block, p, s));
 }
 
+int64_t losa_dense_attn_mass_workspace(const losa_attn_desc* desc) {
+  int32_t nb = 0;
+  if (check_desc(desc, &nb) != LOSA_OK) return -1;
+  return dense_mass_workspace(desc, nb);
+}
+
+losa_status losa_dense_attn_mass(const losa_attn_desc* desc, const void* q, const void* k,
+                                 const void* v, void* o, float* lse, float* mass,
+                                 void* workspace, int64_t workspace_bytes, void* stream) {
+  int32_t nb = 0;
+  losa_status st = check_desc(desc, &nb);
+  if (st != LOSA_OK) return st;
+  if (!q || !k || !v || !o || !mass || !workspace) return LOSA_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(mass, 4) || !aligned(workspace, 256) || (lse && !aligned(lse, 4)))
+    return LOSA_ERR_MISALIGNED;
+  if (workspace_bytes < dense_mass_workspace(desc, nb)) return LOSA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* rowsum = static_cast<float*>(workspace);
+  float* rowref = reinterpret_cast<float*>(static_cast<char*>(workspace) + rowsum_bytes(desc, nb));
+  losa::AttnParams p = base_params(desc, nb);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  if (desc->dtype == LOSA_FP32) {
+    // fp32: the dense pass writes lse (into the workspace when the caller
+    // wants none) and the two-pass mass kernel reads it
+    float* lse_buf = lse ? lse : rowref;
+    p.lse = lse_buf;
+    st = device_status(losa::launch_attn(losa::kDense, desc->dtype, desc->head_dim, desc->block,
+                                         p, s));
+    if (st != LOSA_OK) return st;
+    p.o = nullptr;
+    p.v = nullptr;
+    p.lse = nullptr;
+    p.lse_in = lse_buf;
+    p.mass = mass;
+    return device_status(
+        losa::launch_attn(losa::kMass, desc->dtype, desc->head_dim, desc->block, p, s));
+  }
+  p.lse = lse;
+  p.rowsum = rowsum;
+  p.rowref = rowref;
+  st = device_status(
+      losa::launch_attn(losa::kDenseMass, desc->dtype, desc->head_dim, desc->block, p, s));
+  if (st != LOSA_OK) return st;
+  return device_status(losa::launch_mass_fold(rowsum, rowref, mass, desc->seq_len, nb,
+                                              desc->block, desc->batch * desc->heads, s));
+}
+
 losa_status losa_select(int32_t rows, int32_t nkb, const float* mass, double threshold,
                         int32_t* idx, int32_t* count, void* stream) {
   if (!mass || !idx || !count) return LOSA_ERR_NULL_POINTER;
@@ -140,6 +202,7 @@ const char* losa_status_string(losa_status status) {
     case LOSA_ERR_MISALIGNED: return "pointer alignment below the requirement";
     case LOSA_ERR_DEVICE: return "the HIP runtime rejected a launch";
     case LOSA_ERR_BAD_ARGUMENT: return "invalid argument (scale must be finite and >= 0)";
+    case LOSA_ERR_WORKSPACE: return "workspace smaller than the size the library asks for";
   }
   return "unknown status";
 }

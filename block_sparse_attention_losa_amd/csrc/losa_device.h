@@ -33,6 +33,33 @@ __device__ __forceinline__ constexpr int c_row(int i, int g) {
   return 8 * (i >> 2) + 4 * g + (i & 3);
 }
 
+// The values of x in lanes l mod 32 and l mod 32 + 32 (lower half first),
+// in every lane l, without an LDS round trip: v_permlane32_swap exchanges
+// the upper 32 lanes of its first operand with the lower 32 lanes of its
+// second (lane layout checked with a probe), so with x in both operands the
+// first holds (x_lo, x_lo) and the second (x_hi, x_hi) afterwards.  Written
+// as inline asm with both registers as in/out operands: the compiler's
+// builtin for it returned the first register for both results.  The s_nop
+// covers the VALU-write -> permlane-read hazard on the inputs; fetch-inactive
+// is set in case the exchange ends up in a branch that runs half the wave.
+__device__ __forceinline__ void lane_halves(float x, float& lo, float& hi) {
+  float a = x, b = x;
+  asm("s_nop 1\n\tv_permlane32_swap_b32_e64 %0, %1 fi:1" : "+v"(a), "+v"(b));
+  lo = a;
+  hi = b;
+}
+// x[l mod 32] + x[l mod 32 + 32], the same bits in both lanes of a pair.
+__device__ __forceinline__ float pair_sum(float x) {
+  float lo, hi;
+  lane_halves(x, lo, hi);
+  return lo + hi;
+}
+__device__ __forceinline__ float pair_max(float x) {
+  float lo, hi;
+  lane_halves(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);

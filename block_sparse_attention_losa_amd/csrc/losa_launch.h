@@ -6,7 +6,9 @@
 
 namespace losa {
 
-enum Mode : int { kDense = 0, kSparse = 1, kLse = 2, kMass = 3 };
+// kDenseMass: the dense pass that also writes, per row and key block, the
+// block's share of the row's softmax sum (see attn_bf16.hip) for the mass map.
+enum Mode : int { kDense = 0, kSparse = 1, kLse = 2, kMass = 3, kDenseMass = 4 };
 
 struct AttnParams {
   const void* q;
@@ -18,6 +20,8 @@ struct AttnParams {
   float* lse;            // dense/sparse/lse: [B,H,N] output, may be null (not for kLse)
   const float* lse_in;   // mass: [B,H,N] input
   float* mass;           // mass: [B*H*nb, nb]
+  float* rowsum;         // dense+mass: [B*H, nb, N] log2 block sums (workspace)
+  float* rowref;         // dense+mass: [B*H, N] per-row offsets (workspace)
   int32_t n;             // tokens
   int32_t nb;            // blocks per sequence
   int32_t items;         // B*H*nb work items (one per query block)
@@ -32,6 +36,11 @@ hipError_t launch_attn(int mode, int dtype, int head_dim, int block, const AttnP
 // bf16 kernels (LDS-DMA pipeline); same contract as launch_attn.
 hipError_t launch_attn_bf16(int mode, int head_dim, int block, const AttnParams& p,
                             hipStream_t stream);
+
+// Folds the per-row block sums of the dense+mass pass into the mass map:
+// mass[bh, I, J] = (1/|I|) sum_{i in I} exp2(rowsum[bh, J, i] - rowref[bh, i]).
+hipError_t launch_mass_fold(const float* rowsum, const float* rowref, float* mass, int32_t n,
+                            int32_t nb, int32_t block, int32_t bh_count, hipStream_t stream);
 
 hipError_t launch_select(int32_t rows, int32_t nkb, const float* mass, double tau,
                          int32_t* idx, int32_t* count, hipStream_t stream);

@@ -51,7 +51,8 @@ typedef enum {
   LOSA_ERR_BAD_THRESHOLD = 4,  /* threshold NaN or <= 0                     */
   LOSA_ERR_MISALIGNED = 5,     /* pointer alignment below the requirement   */
   LOSA_ERR_DEVICE = 6,         /* the HIP runtime rejected a launch         */
-  LOSA_ERR_BAD_ARGUMENT = 7    /* other invalid argument (e.g. scale)       */
+  LOSA_ERR_BAD_ARGUMENT = 7,   /* other invalid argument (e.g. scale)       */
+  LOSA_ERR_WORKSPACE = 8       /* workspace smaller than required           */
 } losa_status;
 
 typedef enum { LOSA_BF16 = 0, LOSA_FP32 = 1 } losa_dtype;
@@ -95,6 +96,34 @@ losa_status losa_dense_attn(const losa_attn_desc* desc, const void* q, const voi
 losa_status losa_block_mass(const losa_attn_desc* desc, const void* q, const void* k,
                             const float* lse, float* lse_scratch, float* mass,
                             void* stream);
+
+/*
+ * The construction step in one sweep over the keys: dense attention (as
+ * losa_dense_attn) and the block mass map (as losa_block_mass) of the same
+ * inputs.  The pages measure exact block masses at one early dense step and
+ * put the cost of that step at about one denoising step (mlsanity.com,
+ * "Abstract (arXiv)"; ubos.tech blog, "How It Works in Practice", Phase 1).
+ * Here the dense pass also records, for each row and key block, the block's
+ * share of the row's softmax sum (log2, against a per-row reference) in
+ * `workspace`, and a second, memory-bound kernel folds those into M once the
+ * row sums are final: the scores are computed once, not twice.
+ *   M[b,h,I,J] = (1/|I|) sum_{i in I} sum_{j in J} exp(s_ij - lse_i)
+ * equals the two-pass result up to rounding.
+ * o: output [B,H,N,D]; lse: output [B,H,N] fp32 or NULL; mass: output
+ * [B,H,nb,nb] fp32.
+ * workspace: device memory of at least losa_dense_attn_mass_workspace(desc)
+ *   bytes, 256-byte aligned, owned by the caller; its contents on entry are
+ *   ignored and on return are unspecified (4*B*H*N*(nb+1) bytes plus
+ *   alignment: 0.8 GB for B1 H12 N32760 block 64).  Calls running at the
+ *   same time need separate workspaces.
+ * For LOSA_FP32 the call runs the dense pass and the two-pass mass kernel
+ * (the workspace then holds lse when lse is NULL).
+ * Returns LOSA_ERR_WORKSPACE when workspace_bytes is below the requirement.
+ */
+int64_t losa_dense_attn_mass_workspace(const losa_attn_desc* desc);
+losa_status losa_dense_attn_mass(const losa_attn_desc* desc, const void* q, const void* k,
+                                 const void* v, void* o, float* lse, float* mass,
+                                 void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * Threshold selection (ubos.tech blog, "How It Works in Practice", Phase 2;

@@ -46,8 +46,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in range(8):
-        assert lib.losa_status_string(code)
+    for code in range(9):
+        assert lib.losa_status_string(code) != b"unknown status"
     assert lib.losa_status_string(99) == b"unknown status"
     assert lib.losa_version() >= 100
 
@@ -69,6 +69,9 @@ def test_descriptor_validation(lib, kw, code):
     assert lib.losa_dense_attn(d, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == code
     assert lib.losa_sparse_attn(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == code
     assert lib.losa_block_mass(d, FAKE, FAKE, FAKE, NULL, FAKE, NULL) == code
+    assert lib.losa_dense_attn_mass(d, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 1 << 40,
+                                    NULL) == code
+    assert lib.losa_dense_attn_mass_workspace(d) == -1
 
 
 def test_null_and_alignment(lib):
@@ -85,6 +88,21 @@ def test_null_and_alignment(lib):
     assert lib.losa_block_mass(d, FAKE, FAKE, NULL, NULL, FAKE, NULL) == 1
     assert lib.losa_block_mass(d, FAKE, FAKE, FAKE, NULL, NULL, NULL) == 1
     assert lib.losa_block_mass(d, FAKE, ODD, FAKE, NULL, FAKE, NULL) == 5
+
+
+def test_dense_attn_mass_workspace_and_validation(lib):
+    d = desc(batch=1, heads=12, seq_len=32760, block=64)
+    need = lib.losa_dense_attn_mass_workspace(d)
+    # per-row block sums [B*H, nb, N] (256-byte padded) + per-row offsets [B*H, N]
+    rowsum = 4 * 12 * 512 * 32760
+    assert need == (rowsum + 255) // 256 * 256 + 4 * 12 * 32760
+    assert lib.losa_dense_attn_mass_workspace(None) == -1
+    args = [FAKE, FAKE, FAKE, FAKE, NULL, FAKE]
+    assert lib.losa_dense_attn_mass(d, *args, FAKE, need - 1, NULL) == 8
+    assert lib.losa_dense_attn_mass(d, *args, NULL, need, NULL) == 1
+    assert lib.losa_dense_attn_mass(d, FAKE, FAKE, FAKE, FAKE, NULL, NULL, FAKE, need, NULL) == 1
+    assert lib.losa_dense_attn_mass(d, *args, ctypes.c_void_p(0x10010), need, NULL) == 5
+    assert lib.losa_dense_attn_mass(d, FAKE, FAKE, ODD, FAKE, NULL, FAKE, FAKE, need, NULL) == 5
 
 
 @pytest.mark.parametrize("rows,nkb,tau,code", [

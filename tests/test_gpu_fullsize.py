@@ -2,11 +2,12 @@
 benchmark times, checked on sampled outputs the oracle computes one query
 block at a time, plus properties checked on every output.
 
-Per configuration: dense attention (O, lse), block mass, threshold selection
-and block-sparse attention, on the construction-step inputs (and, for the
-Wan2.1-1.3B layer, on a perturbed later-step input with the frozen lists).
-Tolerances as in the small-size parity tests: mass 1e-5, outputs 2e-2
-max-abs / 2e-3 mean-abs, lse 1e-3, selection bit-identical.
+Per configuration: dense attention (O, lse), block mass (two-pass and the
+one-sweep construction), threshold selection and block-sparse attention, on
+the construction-step inputs (and, for the Wan2.1-1.3B layer, on a perturbed
+later-step input with the frozen lists).  Tolerances as in the small-size
+parity tests: mass 1e-5, outputs 2e-2 max-abs / 2e-3 mean-abs, lse 1e-3,
+selection bit-identical.
 """
 
 import sys
@@ -85,7 +86,15 @@ def _run_config(losa, cid, taus, later_step=None, n_heads_checked=3, seed=0):
     _say(f"[fullsize] config {cid}: dense + block mass on the GPU")
     o, lse = losa.dense_attn(tq, tk, tv, block=blk)
     mass = losa.block_mass(tq, tk, block=blk, lse=lse)
+    _say(f"[fullsize] config {cid}: one-sweep dense + mass on the GPU")
+    o_f, lse_f, mass_f = losa.dense_attn_mass(tq, tk, tv, block=blk)
     torch.cuda.synchronize()
+    assert torch.equal(o_f, o) and torch.equal(lse_f, lse)
+    fdiff = float((mass_f - mass).abs().max())
+    assert fdiff <= MASS_ATOL, (cid, fdiff)
+    mass_fg = mass_f.cpu().numpy()
+    del o_f, lse_f, mass_f
+    torch.cuda.empty_cache()
     o_g, lse_g, mass_g = o.float().cpu().numpy(), lse.cpu().numpy(), mass.cpu().numpy()
 
     # every mass row sums to 1 (fp32 accumulation of ~nb terms)
@@ -107,6 +116,8 @@ def _run_config(losa, cid, taus, later_step=None, n_heads_checked=3, seed=0):
         md = oracle.block_mass(q[b, h], k[b, h], blk, lse=full_lse, qblocks=qbs)
         merr = np.abs(mass_g[b, h, qbs].astype(np.float64) - md).max()
         assert merr <= MASS_ATOL, (cid, b, h, merr)
+        ferr = np.abs(mass_fg[b, h, qbs].astype(np.float64) - md).max()
+        assert ferr <= MASS_ATOL, (cid, b, h, ferr)
 
     results = {}
     for tau in taus:

@@ -97,9 +97,16 @@ def test_pipeline_matches_oracle(losa, name):
     _say(f"[parity] {name}: block_mass")
     mass = losa.block_mass(tq, tk, block=blk, lse=lse)
     mass_own = losa.block_mass(tq, tk, block=blk)  # first pass inside
+    _say(f"[parity] {name}: dense_attn_mass")
+    o_f, lse_f, mass_f = losa.dense_attn_mass(tq, tk, tv, block=blk)
     torch.cuda.synchronize()
     o_g, lse_g, mass_g = _np(o), _np(lse), _np(mass)
     assert np.array_equal(mass_g, _np(mass_own)) or np.abs(mass_g - _np(mass_own)).max() < 1e-7
+    # the one-sweep construction: O and lse from the dense pass's own
+    # arithmetic, masses folded from per-row block sums
+    assert np.array_equal(_np(o_f), o_g) and np.array_equal(_np(lse_f), lse_g)
+    mass_fg = _np(mass_f)
+    assert np.abs(mass_fg - mass_g).max() <= MASS_ATOL
 
     for b in range(cfg.batch):
         for h in range(cfg.heads):
@@ -108,6 +115,8 @@ def test_pipeline_matches_oracle(losa, name):
             md = oracle.block_mass(q[b, h], k[b, h], blk, lse=lsed)
             merr = np.abs(mass_g[b, h].astype(np.float64) - md).max()
             assert merr <= MASS_ATOL, f"{name} mass b{b}h{h} err {merr:.3e}"
+            ferr = np.abs(mass_fg[b, h].astype(np.float64) - md).max()
+            assert ferr <= MASS_ATOL, f"{name} one-sweep mass b{b}h{h} err {ferr:.3e}"
 
     for tau in TAUS:
         _say(f"[parity] {name}: select tau={tau}")
