@@ -10,7 +10,8 @@ Sources (the pages describing LoSA, arXiv 2608.12032):
   * "Summary & Methodology Analysis" and FAQ Q4-Q6 on the legiblepapers page,
   * "What the Researchers Propose" and "How It Works in Practice"
     (Phases 1-3) on the ubos.tech blog post,
-  * "Abstract Summary" on the aitobox blog post.
+  * "Abstract Summary" and "Key Highlights" on the aitobox blog post,
+  * "Key Findings" and "What Comes Next" on the ubos.tech blog post.
 """
 
 from .losa_oracle import (  # noqa: F401
@@ -23,4 +24,7 @@ from .losa_oracle import (  # noqa: F401
     select,
     sparse_attention,
     kept_key_mask,
+    retained_mass,
+    select_rows,
+    block_mask,
 )

@@ -233,3 +233,79 @@ def sparse_attention(q, k, v, idx, count, block, scale=None, qblocks=None):
         o_parts.append(o_blk)
         lse_parts.append(lse_blk)
     return np.concatenate(o_parts), np.concatenate(lse_parts)
+
+
+def retained_mass(q, k, idx, count, block, scale=None, lse=None, qblocks=None):
+    """Share of each query block's dense attention mass that falls on its
+    retained keys, averaged over the block's valid rows:
+
+        R[I] = (1/|I|) * sum_{i in I} sum_{j kept by I} exp(s_ij - lse_i)
+
+    with ``lse`` the dense row log-sum-exp of the same inputs (computed when
+    not given).  On the construction-step inputs R[I] is at least tau by
+    selection; on later-step inputs it measures how much of the attention
+    mass the frozen lists still cover.
+
+    [ubos.tech blog, "Key Findings": the high-mass block set stays stable
+    across denoising steps, so one early calibration serves the whole
+    generation; aitobox blog, "Key Highlights": the high-mass support
+    remains stable across denoising steps.]
+
+    ``idx`` is ``[nb, nb]`` and ``count`` ``[nb]`` for this (batch, head).
+    Returns ``[len(qblocks)]`` float64 (all query blocks by default).
+    """
+    q, k = _f64(q), _f64(k)
+    n = q.shape[0]
+    c = _scale(q.shape[1], scale)
+    nb = num_blocks(n, block)
+    if lse is None:
+        lse = row_lse(q, k, scale)
+    lse = _f64(lse)
+    qblocks = range(nb) if qblocks is None else qblocks
+    out = np.zeros(len(qblocks))
+    for row, qi in enumerate(qblocks):
+        lo, hi = block_rows(qi, n, block)
+        s = c * (q[lo:hi] @ k.T)
+        p = np.exp(s - lse[lo:hi, None])
+        keep = kept_key_mask(idx[qi], count[qi], block, n)
+        out[row] = p[:, keep].sum(axis=1).mean()
+    return out
+
+
+def select_rows(mass, taus):
+    """:func:`select_row` with a threshold of its own for every row of
+    ``mass`` (``[R, nb]``; ``taus`` ``[R]``).
+
+    [ubos.tech blog, "What Comes Next": adapting the retained-mass target per
+    frame or per scene.]
+
+    Returns ``idx`` ``[R, nb]`` int32 (-1 past ``count``) and ``count``.
+    """
+    mass = np.asarray(mass)
+    rows, nb = mass.shape
+    idx = np.full((rows, nb), -1, dtype=np.int32)
+    count = np.zeros(rows, dtype=np.int32)
+    for r in range(rows):
+        kept, cnt = select_row(mass[r], float(taus[r]))
+        idx[r, :cnt] = kept
+        count[r] = cnt
+    return idx, count
+
+
+def block_mask(idx, count, nkb):
+    """The block mask: ``mask[r, j] = 1`` when key block ``j`` is among the
+    first ``count[r]`` entries of ``idx[r]``, else 0 (uint8 ``[R, nkb]``).
+
+    [ubos.tech blog, "How It Works in Practice", Phase 2: the selection
+    yields a mask tensor of shape (heads, query blocks, key blocks) that is
+    stored for reuse.]
+    """
+    idx = np.asarray(idx)
+    count = np.asarray(count).ravel()
+    rows = count.shape[0]
+    idx = idx.reshape(rows, -1)
+    mask = np.zeros((rows, int(nkb)), dtype=np.uint8)
+    for r in range(rows):
+        for j in idx[r, :int(count[r])]:
+            mask[r, int(j)] = 1
+    return mask

@@ -80,3 +80,23 @@ def minimal_sets(masses, tau):
         if best is not None:
             return size, set(best[1])
     return nb, set(range(nb))
+
+
+def retained(q, k, scale, block, idx, count):
+    """R[I] = average over the valid rows i of I of the dense attention
+    probability that row i puts on the keys of the blocks idx[I][:count[I]]."""
+    n = len(q)
+    nb = (n + block - 1) // block
+    _, lse = attention(q, k, [[0.0]] * len(k), scale)
+    out = []
+    for big_i in range(nb):
+        kept = set(int(j) for j in idx[big_i][:count[big_i]])
+        rows = range(big_i * block, min(n, (big_i + 1) * block))
+        total = 0.0
+        for i in rows:
+            for j in range(n):
+                if j // block in kept:
+                    dot = sum(q[i][t] * k[j][t] for t in range(len(q[0])))
+                    total += math.exp(scale * dot - lse[i])
+        out.append(total / len(rows))
+    return out

@@ -61,6 +61,22 @@ MUTANTS = {
         "return lo, lo + int(block)",
         [lambda: pins.test_mass_rows_sum_to_one(250, 64),
          lambda: pins.test_sparse_matches_brute_force(19, 4)]),
+    "retained mass over the full block": (
+        "out[row] = p[:, keep].sum(axis=1).mean()",
+        "out[row] = p[:, keep].sum(axis=1).sum() / block",
+        [lambda: pins.test_retained_mass_matches_brute_force(19, 4)]),
+    "retained mass without the dense normaliser": (
+        "p = np.exp(s - lse[lo:hi, None])\n        keep",
+        "p = np.exp(s)\n        keep",
+        [lambda: pins.test_retained_mass_bounds_and_construction_step()]),
+    "per-row threshold of the wrong row": (
+        "kept, cnt = select_row(mass[r], float(taus[r]))",
+        "kept, cnt = select_row(mass[r], float(taus[r - 1]))",
+        [lambda: pins.test_select_rows_matches_subset_enumeration_per_row(0)]),
+    "mask past count": (
+        "for j in idx[r, :int(count[r])]:",
+        "for j in idx[r, :int(count[r]) + 1]:",
+        [lambda: pins.test_block_mask_worked_example_and_counts()]),
 }
 
 

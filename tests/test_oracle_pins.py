@@ -320,3 +320,83 @@ def test_threshold_retains_mass_end_to_end():
         idx, count = oracle.select(m, tau)
         for i in range(m.shape[0]):
             assert m[i, idx[i, :count[i]]].sum() >= tau
+
+
+# ------------------------------------------- retained mass (drift diagnostic)
+
+@pytest.mark.parametrize("n,block", [(16, 4), (19, 4), (11, 5)])
+def test_retained_mass_matches_brute_force(n, block):
+    rng = np.random.default_rng(100 + n)
+    d = 5
+    q, k = _rand(n, d, 2.0), _rand(n, d, 2.0)
+    nb = oracle.num_blocks(n, block)
+    idx, count = _random_lists(nb, rng)
+    r = oracle.retained_mass(q, k, idx, count, block)
+    br = _brute.retained(q.tolist(), k.tolist(), 1 / math.sqrt(d), block, idx.tolist(),
+                         count.tolist())
+    np.testing.assert_allclose(r, br, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n,block", [(300, 64), (256, 128)])
+def test_retained_mass_is_the_kept_part_of_the_mass_map(n, block):
+    # the same quantity summed per key block instead of per row
+    rng = np.random.default_rng(n)
+    q, k = _rand(n, 16, 3), _rand(n, 16, 3)
+    nb = oracle.num_blocks(n, block)
+    idx, count = _random_lists(nb, rng)
+    m = oracle.block_mass(q, k, block)
+    r = oracle.retained_mass(q, k, idx, count, block)
+    for i in range(nb):
+        assert abs(r[i] - m[i, idx[i, :count[i]]].sum()) < 1e-12
+
+
+def test_retained_mass_bounds_and_construction_step():
+    n, block = 450, 64
+    q, k = _rand(n, 16, 3), _rand(n, 16, 3)
+    nb = oracle.num_blocks(n, block)
+    m = oracle.block_mass(q, k, block)
+    # every block kept: all of the mass
+    idx, count = oracle.select(m, 1.0)
+    np.testing.assert_allclose(oracle.retained_mass(q, k, idx, count, block), 1.0,
+                               rtol=0, atol=1e-12)
+    # lists selected on the same inputs keep at least tau
+    for tau in (0.5, 0.9, 0.99):
+        idx, count = oracle.select(m, tau)
+        assert (oracle.retained_mass(q, k, idx, count, block) >= tau - 1e-12).all()
+    # an empty list keeps nothing
+    count = np.zeros(nb, int)
+    assert (oracle.retained_mass(q, k, idx, count, block) == 0).all()
+
+
+# --------------------------------------------------- per-row thresholds, mask
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_select_rows_matches_subset_enumeration_per_row(seed):
+    rng = np.random.default_rng(300 + seed)
+    rows, nb = 12, 8
+    mass = rng.dirichlet(np.full(nb, 0.7), size=rows)
+    taus = rng.uniform(0.2, 1.1, rows)
+    taus[0], taus[1] = 1.0, 0.01
+    idx, count = oracle.select_rows(mass, taus)
+    for r in range(rows):
+        size, best = _brute.minimal_sets(mass[r], taus[r] if taus[r] < 1 else 2.0)
+        assert count[r] == size, (r, taus[r])
+        assert set(idx[r, :count[r]].tolist()) == best
+    assert count[0] == nb and count[1] == 1 and idx[1, 0] == int(np.argmax(mass[1]))
+
+
+def test_block_mask_worked_example_and_counts():
+    idx = np.array([[2, 0, -1], [1, -1, -1], [0, 1, 2]])
+    count = np.array([2, 1, 3])
+    expect = np.array([[1, 0, 1], [0, 1, 0], [1, 1, 1]], np.uint8)
+    assert np.array_equal(oracle.block_mask(idx, count, 3), expect)
+    rng = np.random.default_rng(8)
+    m = rng.dirichlet(np.full(40, 0.3), size=25)
+    for tau in (0.5, 0.99, 1.0):
+        idx, count = oracle.select(m, tau)
+        mask = oracle.block_mask(idx, count, 40)
+        assert (mask.sum(1) == count).all()
+        for r in range(25):
+            assert set(np.nonzero(mask[r])[0].tolist()) == set(idx[r, :count[r]].tolist())
+        if tau == 1.0:
+            assert (mask == 1).all()
