@@ -8,8 +8,10 @@ block_sparse_attention_losa_amd.build``).
 """
 
 from ._lib import LosaError, LosaLibraryMissing  # noqa: F401
-from .api import (block_mass, dense_attn, dense_attn_mass,  # noqa: F401
-                  dense_attn_mass_workspace_bytes, num_blocks, select, sparse_attn)
+from .api import (block_mask, block_mass, dense_attn, dense_attn_mass,  # noqa: F401
+                  dense_attn_mass_workspace_bytes, num_blocks, retained_mass, select,
+                  select_per_row, sparse_attn)
 
 __all__ = ["dense_attn", "block_mass", "dense_attn_mass", "dense_attn_mass_workspace_bytes",
-           "select", "sparse_attn", "num_blocks", "LosaError", "LosaLibraryMissing"]
+           "select", "select_per_row", "sparse_attn", "block_mask", "retained_mass",
+           "num_blocks", "LosaError", "LosaLibraryMissing"]

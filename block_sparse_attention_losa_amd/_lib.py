@@ -63,6 +63,10 @@ SIGNATURES = {
                                             ctypes.c_int64, _VP]),
     "losa_select": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_double,
                                    _VP, _VP, _VP]),
+    "losa_select_per_row": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _VP, _VP,
+                                           ctypes.c_int32, _VP, _VP, _VP]),
+    "losa_block_mask": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP]),
+    "losa_retained_mass": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP]),
     "losa_sparse_attn": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "losa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "losa_version": (ctypes.c_int32, []),

@@ -138,6 +138,67 @@ def select(mass, threshold: float = 0.99, idx=None, count=None):
     return idx, count
 
 
+def select_per_row(mass, thresholds, rows_per_threshold: int = 1, idx=None, count=None):
+    """Threshold selection with a threshold per group of ``rows_per_threshold``
+    rows of ``mass`` (flattened over its leading axes); ``thresholds`` is a
+    float64 device tensor of ``ceil(rows / rows_per_threshold)`` values.
+    Returns ``(idx, count)`` as :func:`select`."""
+    _check_inputs(mass, thresholds)
+    if mass.dtype != torch.float32 or thresholds.dtype != torch.float64:
+        raise TypeError("mass must be float32 and thresholds float64")
+    nkb = mass.shape[-1]
+    rows = mass.numel() // nkb if nkb else 0
+    if thresholds.numel() < (rows + rows_per_threshold - 1) // max(1, rows_per_threshold):
+        raise ValueError("too few thresholds for the rows")
+    if idx is None:
+        idx = torch.empty(mass.shape, dtype=torch.int32, device=mass.device)
+    if count is None:
+        count = torch.empty(mass.shape[:-1], dtype=torch.int32, device=mass.device)
+    lib = _lib.load()
+    _lib.check("losa_select_per_row", lib.losa_select_per_row(
+        rows, nkb, _ptr(mass), _ptr(thresholds), int(rows_per_threshold), _ptr(idx),
+        _ptr(count), _stream(mass)))
+    return idx, count
+
+
+def block_mask(idx, count, mask=None):
+    """The lists as a uint8 mask shaped like ``idx`` (1 = key block kept)."""
+    _check_inputs(idx, count)
+    if idx.dtype != torch.int32 or count.dtype != torch.int32:
+        raise TypeError("idx and count must be int32")
+    nkb = idx.shape[-1]
+    rows = idx.numel() // nkb if nkb else 0
+    if count.numel() != rows:
+        raise ValueError("count must have one entry per row of idx")
+    if mask is None:
+        mask = torch.empty(idx.shape, dtype=torch.uint8, device=idx.device)
+    lib = _lib.load()
+    _lib.check("losa_block_mask", lib.losa_block_mask(
+        rows, nkb, _ptr(idx), _ptr(count), _ptr(mask), _stream(idx)))
+    return mask
+
+
+def retained_mass(lse_kept, lse_dense, block: int = 64, head_dim: int = 128, retained=None):
+    """Drift diagnostic: per query block, the share of the dense attention
+    mass that the frozen lists cover, from the lse of a sparse pass and of a
+    dense pass on the same inputs (both ``[B, H, N]`` float32).  Returns
+    ``[B, H, nb]`` float32."""
+    _check_inputs(lse_kept, lse_dense)
+    if lse_kept.shape != lse_dense.shape or lse_kept.dim() != 3:
+        raise ValueError("expected two [B, H, N] lse tensors")
+    if lse_kept.dtype != torch.float32 or lse_dense.dtype != torch.float32:
+        raise TypeError("lse tensors must be float32")
+    b, h, n = lse_kept.shape
+    nb = num_blocks(n, block)
+    desc = _lib.AttnDesc(b, h, n, int(head_dim), int(block), _lib.LOSA_BF16, 0.0)
+    if retained is None:
+        retained = torch.empty((b, h, nb), dtype=torch.float32, device=lse_kept.device)
+    lib = _lib.load()
+    _lib.check("losa_retained_mass", lib.losa_retained_mass(
+        desc, _ptr(lse_kept), _ptr(lse_dense), _ptr(retained), _stream(lse_kept)))
+    return retained
+
+
 def sparse_attn(q, k, v, idx, count, block: int = 64, scale=None, o=None, lse=None,
                 want_lse=False):
     """Block-sparse attention over frozen lists; returns ``(o, lse)``."""

@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblosa.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
-HIP_SOURCES = ["attn_bf16.hip", "attn_fwd.hip", "select.hip", "mass_fold.hip"]
+HIP_SOURCES = ["attn_bf16.hip", "attn_fwd.hip", "select.hip", "mass_fold.hip",
+               "frozen_lists.hip"]
 HOST_SOURCES = ["losa_api.cpp"]
 
 ARCH = "gfx950"

@@ -1,0 +1,86 @@
+// Small kernels over the frozen block lists:
+//  * block_mask_kernel -- the lists as a dense mask tensor (query block x key
+//    block, 1 = retained), the form in which the pages store the selection
+//    for reuse (ubos.tech blog, "How It Works in Practice", Phase 2);
+//  * retained_mass_kernel -- how much of a later step's dense attention mass
+//    the frozen lists still cover, from the row log-sum-exps of a sparse pass
+//    (lse') and a dense pass (lse) on the same inputs:
+//      R[I] = (1/|I|) sum_{i in I} exp(lse'_i - lse_i),
+//    since exp(lse'_i - lse_i) = sum_{j kept} exp(s_ij) / sum_j exp(s_ij).
+//    The pages report that the high-mass block set stays stable across
+//    denoising steps (ubos.tech blog, "Key Findings"; aitobox blog, "Key
+//    Highlights"); R measures that on the caller's own inputs.
+// Both are memory-bound; neither allocates.
+#include "losa_device.h"
+#include "losa_launch.h"
+
+namespace losa {
+
+// One wave per row of the mask, four rows per workgroup.  The row is built
+// as byte flags in LDS (zero, then one per listed block; entries outside
+// [0, nkb) and past count are ignored) and written out coalesced.
+__global__ void __launch_bounds__(256) block_mask_kernel(const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ count,
+                                                         uint8_t* __restrict__ mask, int rows,
+                                                         int nkb) {
+  __shared__ unsigned char flags[4][1024];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave;
+  const bool live = row < rows;
+  unsigned char* f = flags[wave];
+  for (int j = lane; j < nkb; j += 64) f[j] = 0;
+  __syncthreads();
+  if (live) {
+    const int c = min(max(count[row], 0), nkb);
+    const int32_t* list = idx + (size_t)row * nkb;
+    for (int t = lane; t < c; t += 64) {
+      const int j = list[t];
+      if ((unsigned)j < (unsigned)nkb) f[j] = 1;
+    }
+  }
+  __syncthreads();
+  if (live) {
+    uint8_t* out = mask + (size_t)row * nkb;
+    for (int j = lane; j < nkb; j += 64) out[j] = f[j];
+  }
+}
+
+// One wave per (batch*head, query block): lane l takes rows l and l + 64 of
+// the block; a butterfly sums them in a fixed order.
+__global__ void __launch_bounds__(256) retained_mass_kernel(const float* __restrict__ lse_kept,
+                                                            const float* __restrict__ lse_dense,
+                                                            float* __restrict__ retained, int n,
+                                                            int nb, int block, int items) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + wave;  // bh * nb + I
+  if (item >= items) return;  // no barriers: whole waves leave together
+  const int bh = item / nb;
+  const int qb = item - bh * nb;
+  const int r0 = qb * block;
+  const int rows = min(block, n - r0);
+  const size_t base = (size_t)bh * n + r0;
+  float acc = 0.f;
+  for (int r = lane; r < rows; r += 64)
+    acc += expf(lse_kept[base + r] - lse_dense[base + r]);
+  acc = wave_sum(acc);
+  if (lane == 0) retained[item] = acc / (float)rows;
+}
+
+hipError_t launch_block_mask(int32_t rows, int32_t nkb, const int32_t* idx, const int32_t* count,
+                             uint8_t* mask, hipStream_t stream) {
+  if (nkb > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(block_mask_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                     idx, count, mask, rows, nkb);
+  return hipGetLastError();
+}
+
+hipError_t launch_retained_mass(const float* lse_kept, const float* lse_dense, float* retained,
+                                int32_t n, int32_t nb, int32_t block, int32_t bh_count,
+                                hipStream_t stream) {
+  const long long items = (long long)bh_count * nb;
+  hipLaunchKernelGGL(retained_mass_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0,
+                     stream, lse_kept, lse_dense, retained, n, nb, block, (int)items);
+  return hipGetLastError();
+}
+
+}  // namespace losa

@@ -166,8 +166,42 @@ losa_status losa_select(int32_t rows, int32_t nkb, const float* mass, double thr
   if (rows < 1 || nkb < 1 || nkb > LOSA_MAX_BLOCKS) return LOSA_ERR_BAD_SHAPE;
   if (std::isnan(threshold) || !(threshold > 0.0)) return LOSA_ERR_BAD_THRESHOLD;
   if (!aligned(mass, 4) || !aligned(idx, 4) || !aligned(count, 4)) return LOSA_ERR_MISALIGNED;
+  return device_status(losa::launch_select(rows, nkb, mass, threshold, nullptr, 1, idx, count,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+losa_status losa_select_per_row(int32_t rows, int32_t nkb, const float* mass,
+                                const double* thresholds, int32_t rows_per_threshold,
+                                int32_t* idx, int32_t* count, void* stream) {
+  if (!mass || !thresholds || !idx || !count) return LOSA_ERR_NULL_POINTER;
+  if (rows < 1 || nkb < 1 || nkb > LOSA_MAX_BLOCKS) return LOSA_ERR_BAD_SHAPE;
+  if (rows_per_threshold < 1) return LOSA_ERR_BAD_ARGUMENT;
+  if (!aligned(mass, 4) || !aligned(thresholds, 8) || !aligned(idx, 4) || !aligned(count, 4))
+    return LOSA_ERR_MISALIGNED;
+  return device_status(losa::launch_select(rows, nkb, mass, 0.0, thresholds, rows_per_threshold,
+                                          idx, count, static_cast<hipStream_t>(stream)));
+}
+
+losa_status losa_block_mask(int32_t rows, int32_t nkb, const int32_t* idx, const int32_t* count,
+                            uint8_t* mask, void* stream) {
+  if (!idx || !count || !mask) return LOSA_ERR_NULL_POINTER;
+  if (rows < 1 || nkb < 1 || nkb > LOSA_MAX_BLOCKS) return LOSA_ERR_BAD_SHAPE;
+  if (!aligned(idx, 4) || !aligned(count, 4)) return LOSA_ERR_MISALIGNED;
   return device_status(
-      losa::launch_select(rows, nkb, mass, threshold, idx, count, static_cast<hipStream_t>(stream)));
+      losa::launch_block_mask(rows, nkb, idx, count, mask, static_cast<hipStream_t>(stream)));
+}
+
+losa_status losa_retained_mass(const losa_attn_desc* desc, const float* lse_kept,
+                               const float* lse_dense, float* retained, void* stream) {
+  int32_t nb = 0;
+  losa_status st = check_desc(desc, &nb);
+  if (st != LOSA_OK) return st;
+  if (!lse_kept || !lse_dense || !retained) return LOSA_ERR_NULL_POINTER;
+  if (!aligned(lse_kept, 4) || !aligned(lse_dense, 4) || !aligned(retained, 4))
+    return LOSA_ERR_MISALIGNED;
+  return device_status(losa::launch_retained_mass(lse_kept, lse_dense, retained, desc->seq_len,
+                                                  nb, desc->block, desc->batch * desc->heads,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 losa_status losa_sparse_attn(const losa_attn_desc* desc, const void* q, const void* k,

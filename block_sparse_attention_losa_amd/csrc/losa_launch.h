@@ -42,7 +42,19 @@ hipError_t launch_attn_bf16(int mode, int head_dim, int block, const AttnParams&
 hipError_t launch_mass_fold(const float* rowsum, const float* rowref, float* mass, int32_t n,
                             int32_t nb, int32_t block, int32_t bh_count, hipStream_t stream);
 
+// taus == nullptr: every row uses tau; otherwise row r uses
+// taus[r / rows_per_tau].
 hipError_t launch_select(int32_t rows, int32_t nkb, const float* mass, double tau,
-                         int32_t* idx, int32_t* count, hipStream_t stream);
+                         const double* taus, int32_t rows_per_tau, int32_t* idx, int32_t* count,
+                         hipStream_t stream);
+
+// mask[r, j] = 1 when j is among idx[r, 0:count[r]], else 0 ([rows, nkb] uint8).
+hipError_t launch_block_mask(int32_t rows, int32_t nkb, const int32_t* idx, const int32_t* count,
+                             uint8_t* mask, hipStream_t stream);
+
+// retained[bh, I] = (1/|I|) sum_{i in I} exp(lse_kept[bh, i] - lse_dense[bh, i]).
+hipError_t launch_retained_mass(const float* lse_kept, const float* lse_dense, float* retained,
+                                int32_t n, int32_t nb, int32_t block, int32_t bh_count,
+                                hipStream_t stream);
 
 }  // namespace losa

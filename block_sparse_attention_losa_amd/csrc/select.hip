@@ -9,7 +9,8 @@
 // prefix sum in sorted order finds the first position where the running mass
 // reaches the threshold.  Float64 sums of float32 masses >= 2^-30 are exact
 // below 1 under any association, so the parallel scan decides exactly like
-// a sequential accumulation.
+// a sequential accumulation.  The threshold is one value for every row, or
+// (per-row variant) taus[row / rows_per_tau] read from device memory.
 #include "losa_device.h"
 #include "losa_launch.h"
 
@@ -18,11 +19,14 @@ namespace losa {
 template <int E>
 __global__ void __launch_bounds__(256) select_kernel(const float* __restrict__ mass, int rows,
                                                      int nkb, double tau,
+                                                     const double* __restrict__ taus,
+                                                     int rows_per_tau,
                                                      int32_t* __restrict__ idx,
                                                      int32_t* __restrict__ count) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + wave;
   if (row >= rows) return;  // no barriers below: whole waves leave together
+  if (taus != nullptr) tau = taus[row / rows_per_tau];
   const float* __restrict__ m = mass + (size_t)row * nkb;
 
   unsigned long long key[E];
@@ -110,19 +114,25 @@ __global__ void __launch_bounds__(256) select_kernel(const float* __restrict__ m
   if (lane == 0) count[row] = cnt;
 }
 
-hipError_t launch_select(int32_t rows, int32_t nkb, const float* mass, double tau, int32_t* idx,
-                         int32_t* count, hipStream_t stream) {
+hipError_t launch_select(int32_t rows, int32_t nkb, const float* mass, double tau,
+                         const double* taus, int32_t rows_per_tau, int32_t* idx, int32_t* count,
+                         hipStream_t stream) {
   const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   if (nkb <= 64) {
-    hipLaunchKernelGGL(select_kernel<1>, grid, block, 0, stream, mass, rows, nkb, tau, idx, count);
+    hipLaunchKernelGGL(select_kernel<1>, grid, block, 0, stream, mass, rows, nkb, tau, taus,
+                       rows_per_tau, idx, count);
   } else if (nkb <= 128) {
-    hipLaunchKernelGGL(select_kernel<2>, grid, block, 0, stream, mass, rows, nkb, tau, idx, count);
+    hipLaunchKernelGGL(select_kernel<2>, grid, block, 0, stream, mass, rows, nkb, tau, taus,
+                       rows_per_tau, idx, count);
   } else if (nkb <= 256) {
-    hipLaunchKernelGGL(select_kernel<4>, grid, block, 0, stream, mass, rows, nkb, tau, idx, count);
+    hipLaunchKernelGGL(select_kernel<4>, grid, block, 0, stream, mass, rows, nkb, tau, taus,
+                       rows_per_tau, idx, count);
   } else if (nkb <= 512) {
-    hipLaunchKernelGGL(select_kernel<8>, grid, block, 0, stream, mass, rows, nkb, tau, idx, count);
+    hipLaunchKernelGGL(select_kernel<8>, grid, block, 0, stream, mass, rows, nkb, tau, taus,
+                       rows_per_tau, idx, count);
   } else if (nkb <= 1024) {
-    hipLaunchKernelGGL(select_kernel<16>, grid, block, 0, stream, mass, rows, nkb, tau, idx, count);
+    hipLaunchKernelGGL(select_kernel<16>, grid, block, 0, stream, mass, rows, nkb, tau, taus,
+                       rows_per_tau, idx, count);
   } else {
     return hipErrorInvalidValue;
   }

@@ -142,6 +142,48 @@ losa_status losa_select(int32_t rows, int32_t nkb, const float* mass, double thr
                         int32_t* idx, int32_t* count, void* stream);
 
 /*
+ * losa_select with a threshold per row or per group of rows, for retained-
+ * mass targets that vary by head or by query block (ubos.tech blog, "What
+ * Comes Next": adapting the retained-mass target per frame or scene).  Row r
+ * uses thresholds[r / rows_per_threshold]: with the [B,H,nb,nb] mass map,
+ * rows_per_threshold = nb gives one threshold per (b,h) and 1 one per query
+ * block.  thresholds: device array of ceil(rows / rows_per_threshold)
+ * doubles, 8-byte aligned.  The values are read on the device and so are not
+ * validated: >= 1 (or NaN) keeps every block, <= 0 keeps one.
+ * Other arguments and results as losa_select.  rows_per_threshold >= 1.
+ */
+losa_status losa_select_per_row(int32_t rows, int32_t nkb, const float* mass,
+                                const double* thresholds, int32_t rows_per_threshold,
+                                int32_t* idx, int32_t* count, void* stream);
+
+/*
+ * The frozen lists as a mask tensor, the form in which the pages store the
+ * selection for reuse (ubos.tech blog, "How It Works in Practice", Phase 2:
+ * a mask of shape (heads, query blocks, key blocks)).
+ *   mask[r, j] = 1 if j is among idx[r, 0:count[r]], else 0.
+ * idx: [rows, nkb] int32, count: [rows] int32 (as from losa_select; entries
+ * outside [0, nkb) are ignored, count is clamped to [0, nkb]);
+ * mask: output [rows, nkb] uint8, no alignment needed.
+ */
+losa_status losa_block_mask(int32_t rows, int32_t nkb, const int32_t* idx, const int32_t* count,
+                            uint8_t* mask, void* stream);
+
+/*
+ * Drift diagnostic of the frozen lists: the share of a later step's dense
+ * attention mass that the lists still cover, per query block.  The pages
+ * report that the high-mass block set stays stable across denoising steps
+ * (ubos.tech blog, "Key Findings"; aitobox blog, "Key Highlights"); this
+ * measures it without a mass pass:
+ *   R[b,h,I] = (1/|I|) sum_{i in I} exp(lse'_i - lse_i)
+ *            = (1/|I|) sum_{i in I} sum_{j kept} exp(s_ij - lse_i),
+ * lse_kept: the lse output [B,H,N] of losa_sparse_attn on the step's inputs;
+ * lse_dense: the lse output [B,H,N] of losa_dense_attn on the same inputs;
+ * retained: output [B,H,nb] fp32.  A query block with an empty list gets 0.
+ */
+losa_status losa_retained_mass(const losa_attn_desc* desc, const float* lse_kept,
+                               const float* lse_dense, float* retained, void* stream);
+
+/*
  * Block-sparse attention over frozen block lists (ubos.tech blog, "How It
  * Works in Practice", Phase 3; legiblepapers, "Summary & Methodology
  * Analysis": later steps attend only to the retained keys).  For query

@@ -120,6 +120,24 @@ def test_select_null_and_alignment(lib):
     assert lib.losa_select(4, 16, ctypes.c_void_p(0x10001), 0.99, FAKE, FAKE, NULL) == 5
 
 
+def test_per_row_select_mask_and_retained_validation(lib):
+    d = desc()
+    assert lib.losa_select_per_row(4, 16, FAKE, NULL, 1, FAKE, FAKE, NULL) == 1
+    assert lib.losa_select_per_row(4, 16, FAKE, FAKE, 0, FAKE, FAKE, NULL) == 7
+    assert lib.losa_select_per_row(0, 16, FAKE, FAKE, 1, FAKE, FAKE, NULL) == 2
+    assert lib.losa_select_per_row(4, 1025, FAKE, FAKE, 1, FAKE, FAKE, NULL) == 2
+    assert lib.losa_select_per_row(4, 16, FAKE, ctypes.c_void_p(0x10004), 1, FAKE, FAKE,
+                                   NULL) == 5
+    assert lib.losa_block_mask(4, 16, NULL, FAKE, FAKE, NULL) == 1
+    assert lib.losa_block_mask(4, 16, FAKE, FAKE, NULL, NULL) == 1
+    assert lib.losa_block_mask(4, 0, FAKE, FAKE, FAKE, NULL) == 2
+    assert lib.losa_block_mask(4, 16, ctypes.c_void_p(0x10002), FAKE, FAKE, NULL) == 5
+    assert lib.losa_retained_mass(None, FAKE, FAKE, FAKE, NULL) == 1
+    assert lib.losa_retained_mass(d, NULL, FAKE, FAKE, NULL) == 1
+    assert lib.losa_retained_mass(d, FAKE, FAKE, ctypes.c_void_p(0x10002), NULL) == 5
+    assert lib.losa_retained_mass(desc(block=32), FAKE, FAKE, FAKE, NULL) == 2
+
+
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(_lib.LosaLibraryMissing):
