@@ -240,6 +240,19 @@ def main():
     two_mass_ms = [e[1].elapsed_time(e[2]) for e in two]
     mass_gap = float((mass2 - mass).abs().max())
 
+    # drift of the frozen lists: share of each later step's dense attention
+    # mass they still cover, at the first and the last later step
+    drift = {}
+    for name, pos in (("first_later_step", 0), ("last_later_step", len(later) - 1)):
+        q, k, v = later[pos]
+        _, lse_d = losa.dense_attn(q, k, v, block=blk)
+        _, lse_k = losa.sparse_attn(q, k, v, idx, count, block=blk, want_lse=True)
+        r = losa.retained_mass(lse_k, lse_d, block=blk, head_dim=d).cpu().numpy()
+        drift[name] = {"step": later_steps[pos], "mean": round(float(r.mean()), 5),
+                       "p1": round(float(np.percentile(r, 1)), 5),
+                       "min": round(float(r.min()), 5)}
+        del lse_d, lse_k
+
     cnt_h = count.cpu().numpy()
     idx_h = idx.cpu().numpy()
     f = float(cnt_h.sum()) / (b * h * nb * nb)
@@ -282,6 +295,7 @@ def main():
                             "two_pass_dense": round(float(np.mean(two_dense_ms)), 4),
                             "two_pass_block_mass": round(float(np.mean(two_mass_ms)), 4),
                             "max_mass_gap_one_sweep_vs_two_pass": mass_gap},
+        "retained_mass": drift,
         "kernel_sha": kernel_hash(),
     }
     if not args.no_cpu_baseline:

@@ -156,6 +156,20 @@ def _run_config(losa, cid, taus, later_step=None, n_heads_checked=3, seed=0):
             err = np.abs(so_g[b, h, r_].astype(np.float64) - ro)
             assert err.max() <= O_MAX and err.mean() <= O_MEAN, (cid, tau, b, h, err.max())
             assert np.abs(slse_g[b, h, r_] - rl).max() <= LSE_ATOL
+        if later_step is not None:
+            # drift diagnostic on the later step: share of its dense mass the
+            # frozen lists cover, against the oracle on the sampled heads
+            _, lse_d = losa.dense_attn(sq, sk, sv, block=blk)
+            ret = losa.retained_mass(slse, lse_d, block=blk, head_dim=cfg.head_dim)
+            ret_g = ret.cpu().numpy()
+            for b, h in heads:
+                qbs = _sample_blocks(cfg, rng, k=2)
+                ref = oracle.retained_mass(qh[b, h], kh[b, h], idx_g[b, h], cnt_g[b, h], blk,
+                                           qblocks=qbs)
+                assert np.abs(ret_g[b, h, qbs] - ref).max() <= 2e-3, (cid, b, h)
+            _say(f"[fullsize] config {cid}: retained mass at step {later_step}: "
+                 f"mean {ret_g.mean():.4f}, min {ret_g.min():.4f}")
+            del lse_d, ret
         results[tau] = float(cnt_g.sum()) / cnt_g.size / nb
         _say(f"[fullsize] config {cid}: tau {tau} kept fraction {results[tau]:.4f}")
     del tq, tk, tv, o, lse, mass
