@@ -164,6 +164,8 @@ def main():
     mass2 = torch.empty_like(mass)
     ws = torch.empty(losa.dense_attn_mass_workspace_bytes(tq3, blk), dtype=torch.uint8,
                      device=dev)
+    plan = losa.sparse_plan(torch.zeros((b, h, nb), dtype=torch.int32, device=dev), block=blk,
+                            head_dim=d)
     idx = torch.empty((b, h, nb, nb), dtype=torch.int32, device=dev)
     count = torch.empty((b, h, nb), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
@@ -173,18 +175,20 @@ def main():
 
     def one_step(record):
         marks = {}
-        e = [ev() for _ in range(3)]
+        e = [ev() for _ in range(4)]
         e[0].record()
         losa.dense_attn_mass(tq3, tk3, tv3, block=blk, o=o_dense, lse=lse, mass=mass,
                              workspace=ws)
         e[1].record()
         losa.select(mass, tau, idx=idx, count=count)
         e[2].record()
+        losa.sparse_plan(count, block=blk, head_dim=d, plan=plan)
+        e[3].record()
         sp = []
         for (q, k, v) in later:
             s0, s1 = ev(), ev()
             s0.record()
-            losa.sparse_attn(q, k, v, idx, count, block=blk, o=o)
+            losa.sparse_attn(q, k, v, idx, count, block=blk, o=o, plan=plan)
             s1.record()
             sp.append((s0, s1))
         if record is not None:
@@ -207,6 +211,7 @@ def main():
 
     fused_ms = [r[0][0].elapsed_time(r[0][1]) for r in recs]
     select_ms = [r[0][1].elapsed_time(r[0][2]) for r in recs]
+    plan_ms = [r[0][2].elapsed_time(r[0][3]) for r in recs]
     sparse_ms = [a.elapsed_time(z) for r in recs for (a, z) in r[1]]
     sparse_mean = float(np.mean(sparse_ms))
 
@@ -222,6 +227,19 @@ def main():
             dense_later.append((s0, s1))
         torch.cuda.synchronize()
     dense_later_ms = [a.elapsed_time(z) for (a, z) in dense_later]
+
+    # the same sparse calls without the plan (default head-major order)
+    unplanned = []
+    if not args.no_dense:
+        log("[bench] sparse kernel without the plan")
+        for (q, k, v) in later:
+            s0, s1 = ev(), ev()
+            s0.record()
+            losa.sparse_attn(q, k, v, idx, count, block=blk, o=o)
+            s1.record()
+            unplanned.append((s0, s1))
+        torch.cuda.synchronize()
+    unplanned_ms = [a.elapsed_time(z) for (a, z) in unplanned]
 
     # the two-pass construction (dense pass with lse, then the mass pass) on
     # the same step-3 input, for comparison with the one-sweep path
@@ -277,7 +295,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": b, "heads": h, "seq_len": n, "head_dim": d,
                    "block": blk, "tau": tau, "later_steps_per_step": len(later),
-                   "step": "one-sweep dense+mass and select on step 3, sparse on each later step"},
+                   "step": "one-sweep dense+mass, select and plan on step 3, planned sparse on each later step"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
@@ -287,11 +305,13 @@ def main():
         "ideal_speedup": round(1.0 / f, 3),
         "speedup_bar": round(0.85 / f, 3),
         "sparse_ms_median": round(float(np.median(sparse_ms)), 4),
+        "sparse_ms_without_plan": round(float(np.mean(unplanned_ms)), 4) if unplanned_ms else None,
         "sparse_kept_tflop": round(flops / 1e12, 4),
         "dense_ms_per_call": round(dense_mean, 4) if dense_mean else None,
         "dense_tflops": round(dflops / (dense_mean * 1e-3) / 1e12, 1) if dense_mean else None,
         "construction_ms": {"dense_attn_mass": round(float(np.mean(fused_ms)), 4),
                             "select": round(float(np.mean(select_ms)), 4),
+                            "sparse_plan": round(float(np.mean(plan_ms)), 4),
                             "two_pass_dense": round(float(np.mean(two_dense_ms)), 4),
                             "two_pass_block_mass": round(float(np.mean(two_mass_ms)), 4),
                             "max_mass_gap_one_sweep_vs_two_pass": mass_gap},

@@ -68,6 +68,10 @@ SIGNATURES = {
     "losa_block_mask": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP]),
     "losa_retained_mass": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP]),
     "losa_sparse_attn": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "losa_sparse_plan_size": (ctypes.c_int64, [_DESC]),
+    "losa_sparse_plan": (ctypes.c_int, [_DESC, _VP, _VP, ctypes.c_int64, _VP]),
+    "losa_sparse_attn_planned": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                                _VP]),
     "losa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "losa_version": (ctypes.c_int32, []),
 }

@@ -199,9 +199,31 @@ def retained_mass(lse_kept, lse_dense, block: int = 64, head_dim: int = 128, ret
     return retained
 
 
+def sparse_plan(count, block: int = 64, head_dim: int = 128, plan=None):
+    """Launch plan for :func:`sparse_attn` over lists with these counts
+    (``[B, H, nb]`` int32): the work items longest-first.  Made once per set
+    of frozen lists; returns an int32 device tensor."""
+    _check_inputs(count)
+    if count.dtype != torch.int32 or count.dim() != 3:
+        raise TypeError("count must be an int32 [B, H, nb] tensor")
+    b, h, nb = count.shape
+    desc = _lib.AttnDesc(b, h, nb * int(block), int(head_dim), int(block), _lib.LOSA_BF16, 0.0)
+    lib = _lib.load()
+    size = lib.losa_sparse_plan_size(desc)
+    if size < 0:
+        raise ValueError("unsupported shape for sparse_plan")
+    if plan is None:
+        plan = torch.empty(size // 4, dtype=torch.int32, device=count.device)
+    _lib.check("losa_sparse_plan", lib.losa_sparse_plan(
+        desc, _ptr(count), _ptr(plan), plan.numel() * 4, _stream(count)))
+    return plan
+
+
 def sparse_attn(q, k, v, idx, count, block: int = 64, scale=None, o=None, lse=None,
-                want_lse=False):
-    """Block-sparse attention over frozen lists; returns ``(o, lse)``."""
+                want_lse=False, plan=None):
+    """Block-sparse attention over frozen lists; returns ``(o, lse)``.  With
+    ``plan`` (from :func:`sparse_plan` on the same counts) the work runs in
+    the plan's order; the results are the same."""
     _check_inputs(q, k, v, idx, count)
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share shape and dtype")
@@ -217,6 +239,14 @@ def sparse_attn(q, k, v, idx, count, block: int = 64, scale=None, o=None, lse=No
     if lse is None and want_lse:
         lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
     lib = _lib.load()
+    if plan is not None:
+        _check_inputs(q, plan)
+        if plan.dtype != torch.int32:
+            raise TypeError("plan must be int32")
+        _lib.check("losa_sparse_attn_planned", lib.losa_sparse_attn_planned(
+            desc, _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(count), _ptr(plan), _ptr(o),
+            _ptr(lse), _stream(q)))
+        return o, lse
     _lib.check("losa_sparse_attn", lib.losa_sparse_attn(
         desc, _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(count), _ptr(o), _ptr(lse),
         _stream(q)))

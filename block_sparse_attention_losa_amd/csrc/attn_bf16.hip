@@ -163,8 +163,12 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnParams p) {
   const int nb = p.nb, N = p.n;
   const int bh_count = p.items / nb;
   const int wph = (nb + G::kQPW - 1) / G::kQPW;  // workgroups per (batch, head)
-  const int item = xcd_item(blockIdx.x, wph, bh_count);
-  if (item < 0) return;  // padding of the XCD-aware grid
+  // a plan (sparse only) gives the item of each workgroup directly: items
+  // sorted by descending cost and dealt round-robin to the XCDs in dispatch
+  // order, so every XCD gets the same mix and starts with its longest items
+  const int item = p.order != nullptr ? p.order[blockIdx.x] : xcd_item(blockIdx.x, wph, bh_count);
+  // padding of the XCD-aware grid; a plan entry outside the items is ignored
+  if (item < 0 || item >= wph * bh_count) return;
   const int bh = item / wph;
   const int w = item - bh * wph;
   const size_t head_off = (size_t)bh * (size_t)N * D;
@@ -528,8 +532,8 @@ hipError_t launch_b(const AttnParams& p, hipStream_t stream) {
                                                G::kLdsBytes);
   if (attr != hipSuccess) return attr;
   const int wph = (p.nb + G::kQPW - 1) / G::kQPW;
-  hipLaunchKernelGGL(kern, dim3(xcd_grid(wph, p.items / p.nb)), dim3(256), G::kLdsBytes, stream,
-                     p);
+  const int grid = p.order != nullptr ? wph * (p.items / p.nb) : xcd_grid(wph, p.items / p.nb);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), G::kLdsBytes, stream, p);
   return hipGetLastError();
 }
 

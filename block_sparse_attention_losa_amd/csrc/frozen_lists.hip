@@ -9,8 +9,15 @@
 //    since exp(lse'_i - lse_i) = sum_{j kept} exp(s_ij) / sum_j exp(s_ij).
 //    The pages report that the high-mass block set stays stable across
 //    denoising steps (ubos.tech blog, "Key Findings"; aitobox blog, "Key
-//    Highlights"); R measures that on the caller's own inputs.
-// Both are memory-bound; neither allocates.
+//    Highlights"); R measures that on the caller's own inputs;
+//  * sparse_plan_kernel -- a dispatch order for the sparse kernel, made once
+//    per set of frozen lists: the work items sorted by descending cost so
+//    that, dealt round-robin to the XCDs in dispatch order, every XCD gets
+//    the same mix of long and short items and runs its longest ones first.
+//    Per-head kept fractions range from a few percent to all blocks, and in
+//    the default head-major order the last items to start are often long
+//    ones, leaving the chip part-idle at the end.
+// All are memory-bound or tiny; none allocates.
 #include "losa_device.h"
 #include "losa_launch.h"
 
@@ -64,6 +71,54 @@ __global__ void __launch_bounds__(256) retained_mass_kernel(const float* __restr
     acc += expf(lse_kept[base + r] - lse_dense[base + r]);
   acc = wave_sum(acc);
   if (lane == 0) retained[item] = acc / (float)rows;
+}
+
+// One workgroup: a counting sort of the items by cost, descending.  Cost of
+// item (bh, w) = the largest count among query blocks w*qpw .. w*qpw+qpw-1
+// (clamped to [0, nb]); it tracks the item's tile count, the length of the
+// union of those lists.  Items of equal cost land in an unspecified order
+// (LDS atomics), which changes which workgroup runs an item, never its
+// result.
+__global__ void __launch_bounds__(1024) sparse_plan_kernel(const int32_t* __restrict__ count,
+                                                           int nb, int qpw, int n_items, int wph,
+                                                           int32_t* __restrict__ order) {
+  __shared__ int hist[1025];
+  const int tid = threadIdx.x;
+  for (int c = tid; c <= nb; c += 1024) hist[c] = 0;
+  __syncthreads();
+  auto cost_of = [&](int item) -> int {
+    const int bh = item / wph;
+    const int w = item - bh * wph;
+    const int q0 = w * qpw;
+    int c = 0;
+    for (int q = q0; q < min(nb, q0 + qpw); ++q)
+      c = max(c, min(max(count[(size_t)bh * nb + q], 0), nb));
+    return c;
+  };
+  for (int item = tid; item < n_items; item += 1024) atomicAdd(&hist[cost_of(item)], 1);
+  __syncthreads();
+  if (tid == 0) {  // exclusive prefix, highest cost first
+    int run = 0;
+    for (int c = nb; c >= 0; --c) {
+      const int h = hist[c];
+      hist[c] = run;
+      run += h;
+    }
+  }
+  __syncthreads();
+  for (int item = tid; item < n_items; item += 1024) {
+    const int pos = atomicAdd(&hist[cost_of(item)], 1);
+    order[pos] = item;
+  }
+}
+
+hipError_t launch_sparse_plan(const int32_t* count, int32_t nb, int32_t qpw, int32_t bh_count,
+                              int32_t* order, hipStream_t stream) {
+  if (nb > 1024 || qpw < 1) return hipErrorInvalidValue;
+  const int wph = (nb + qpw - 1) / qpw;
+  hipLaunchKernelGGL(sparse_plan_kernel, dim3(1), dim3(1024), 0, stream, count, nb, qpw,
+                     bh_count * wph, wph, order);
+  return hipGetLastError();
 }
 
 hipError_t launch_block_mask(int32_t rows, int32_t nkb, const int32_t* idx, const int32_t* count,

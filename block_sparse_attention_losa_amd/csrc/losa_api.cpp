@@ -53,6 +53,14 @@ int64_t dense_mass_workspace(const losa_attn_desc* d, int32_t nb) {
   return rowsum_bytes(d, nb) + int64_t{4} * d->batch * d->heads * d->seq_len;
 }
 
+// Sparse work items: one per 128 query rows of each (b, h), i.e. per pair of
+// 64-token query blocks or per 128-token block.
+int32_t blocks_per_item(const losa_attn_desc* d) { return d->block == 64 ? 2 : 1; }
+int64_t plan_items(const losa_attn_desc* d, int32_t nb) {
+  const int32_t qpw = blocks_per_item(d);
+  return int64_t{d->batch} * d->heads * ((nb + qpw - 1) / qpw);
+}
+
 }  // namespace
 
 extern "C" {
@@ -222,6 +230,50 @@ losa_status losa_sparse_attn(const losa_attn_desc* desc, const void* q, const vo
   p.cnt = count;
   p.o = o;
   p.lse = lse;
+  return device_status(losa::launch_attn(losa::kSparse, desc->dtype, desc->head_dim, desc->block,
+                                         p, static_cast<hipStream_t>(stream)));
+}
+
+int64_t losa_sparse_plan_size(const losa_attn_desc* desc) {
+  int32_t nb = 0;
+  if (check_desc(desc, &nb) != LOSA_OK) return -1;
+  return 4 * plan_items(desc, nb);
+}
+
+losa_status losa_sparse_plan(const losa_attn_desc* desc, const int32_t* count, int32_t* plan,
+                             int64_t plan_bytes, void* stream) {
+  int32_t nb = 0;
+  losa_status st = check_desc(desc, &nb);
+  if (st != LOSA_OK) return st;
+  if (!count || !plan) return LOSA_ERR_NULL_POINTER;
+  if (!aligned(count, 4) || !aligned(plan, 4)) return LOSA_ERR_MISALIGNED;
+  if (plan_bytes < 4 * plan_items(desc, nb)) return LOSA_ERR_WORKSPACE;
+  return device_status(losa::launch_sparse_plan(count, nb, blocks_per_item(desc),
+                                                desc->batch * desc->heads, plan,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+losa_status losa_sparse_attn_planned(const losa_attn_desc* desc, const void* q, const void* k,
+                                     const void* v, const int32_t* idx, const int32_t* count,
+                                     const int32_t* plan, void* o, float* lse, void* stream) {
+  if (plan == nullptr) return LOSA_ERR_NULL_POINTER;
+  if (!aligned(plan, 4)) return LOSA_ERR_MISALIGNED;
+  int32_t nb = 0;
+  losa_status st = check_desc(desc, &nb);
+  if (st != LOSA_OK) return st;
+  if (!q || !k || !v || !o || !idx || !count) return LOSA_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(idx, 4) || !aligned(count, 4) || (lse && !aligned(lse, 4)))
+    return LOSA_ERR_MISALIGNED;
+  losa::AttnParams p = base_params(desc, nb);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.idx = idx;
+  p.cnt = count;
+  p.o = o;
+  p.lse = lse;
+  if (desc->dtype == LOSA_BF16) p.order = plan;  // the fp32 kernel keeps its own order
   return device_status(losa::launch_attn(losa::kSparse, desc->dtype, desc->head_dim, desc->block,
                                          p, static_cast<hipStream_t>(stream)));
 }

@@ -22,6 +22,7 @@ struct AttnParams {
   float* mass;           // mass: [B*H*nb, nb]
   float* rowsum;         // dense+mass: [B*H, nb, N] log2 block sums (workspace)
   float* rowref;         // dense+mass: [B*H, N] per-row offsets (workspace)
+  const int32_t* order;  // sparse: workgroup b runs work item order[b] (a plan), or null
   int32_t n;             // tokens
   int32_t nb;            // blocks per sequence
   int32_t items;         // B*H*nb work items (one per query block)
@@ -47,6 +48,12 @@ hipError_t launch_mass_fold(const float* rowsum, const float* rowref, float* mas
 hipError_t launch_select(int32_t rows, int32_t nkb, const float* mass, double tau,
                          const double* taus, int32_t rows_per_tau, int32_t* idx, int32_t* count,
                          hipStream_t stream);
+
+// Dispatch order for the sparse kernel: the work items (bh * wph + w, one per
+// group of qpw query blocks) sorted by descending cost, cost = the largest
+// count among the group's query blocks.  order: [bh_count * wph] int32.
+hipError_t launch_sparse_plan(const int32_t* count, int32_t nb, int32_t qpw, int32_t bh_count,
+                              int32_t* order, hipStream_t stream);
 
 // mask[r, j] = 1 when j is among idx[r, 0:count[r]], else 0 ([rows, nkb] uint8).
 hipError_t launch_block_mask(int32_t rows, int32_t nkb, const int32_t* idx, const int32_t* count,

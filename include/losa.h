@@ -200,6 +200,32 @@ losa_status losa_sparse_attn(const losa_attn_desc* desc, const void* q, const vo
                              const void* v, const int32_t* idx, const int32_t* count,
                              void* o, float* lse, void* stream);
 
+/*
+ * Launch plan for block-sparse attention over a fixed set of frozen lists.
+ * The lists do not change after the construction step (mlsanity.com,
+ * "Abstract (arXiv)": index freezing; legiblepapers, FAQ Q6), and neither
+ * does the work they imply, so the order in which the GPU should run it can
+ * be fixed once too: per-head kept fractions range from a few percent to
+ * every block, and running the work items longest-first, dealt evenly over
+ * the chip's 8 XCDs, keeps all compute units busy to the end.
+ * losa_sparse_plan writes that order (int32, losa_sparse_plan_size(desc)
+ * bytes, 4-byte aligned, caller-owned) from count [B,H,nb]; only count is
+ * read.  Recompute it whenever count changes.  Returns LOSA_ERR_WORKSPACE
+ * when plan_bytes is below the size.  Items of equal cost may be ordered
+ * differently from call to call; results do not depend on the order.
+ * losa_sparse_attn_planned computes exactly what losa_sparse_attn computes
+ * (bit-identical outputs) in the plan's order.  The plan is trusted like
+ * idx/count: it must come from losa_sparse_plan for the same desc and count
+ * (entries outside the valid range are skipped, leaving those rows
+ * unwritten).  For LOSA_FP32 the plan is ignored.
+ */
+int64_t losa_sparse_plan_size(const losa_attn_desc* desc);
+losa_status losa_sparse_plan(const losa_attn_desc* desc, const int32_t* count, int32_t* plan,
+                             int64_t plan_bytes, void* stream);
+losa_status losa_sparse_attn_planned(const losa_attn_desc* desc, const void* q, const void* k,
+                                     const void* v, const int32_t* idx, const int32_t* count,
+                                     const int32_t* plan, void* o, float* lse, void* stream);
+
 /* Static text for a status code. */
 const char* losa_status_string(losa_status status);
 

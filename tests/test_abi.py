@@ -138,6 +138,25 @@ def test_per_row_select_mask_and_retained_validation(lib):
     assert lib.losa_retained_mass(desc(block=32), FAKE, FAKE, FAKE, NULL) == 2
 
 
+def test_sparse_plan_validation(lib):
+    d = desc(batch=1, heads=12, seq_len=32760, block=64)
+    assert lib.losa_sparse_plan_size(d) == 4 * 12 * 256      # 128-row items
+    assert lib.losa_sparse_plan_size(desc(seq_len=118800, block=128, heads=24)) == 4 * 24 * 929
+    assert lib.losa_sparse_plan_size(None) == -1
+    need = lib.losa_sparse_plan_size(d)
+    assert lib.losa_sparse_plan(d, NULL, FAKE, need, NULL) == 1
+    assert lib.losa_sparse_plan(d, FAKE, NULL, need, NULL) == 1
+    assert lib.losa_sparse_plan(d, FAKE, ctypes.c_void_p(0x10002), need, NULL) == 5
+    assert lib.losa_sparse_plan(d, FAKE, FAKE, need - 4, NULL) == 8
+    assert lib.losa_sparse_plan(desc(block=32), FAKE, FAKE, need, NULL) == 2
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE]
+    assert lib.losa_sparse_attn_planned(d, *args, NULL, FAKE, NULL, NULL) == 1
+    assert lib.losa_sparse_attn_planned(d, *args, ctypes.c_void_p(0x10002), FAKE, NULL,
+                                        NULL) == 5
+    assert lib.losa_sparse_attn_planned(d, *args, FAKE, NULL, NULL, NULL) == 1
+    assert lib.losa_sparse_attn_planned(desc(head_dim=96), *args, FAKE, FAKE, NULL, NULL) == 2
+
+
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(_lib.LosaLibraryMissing):

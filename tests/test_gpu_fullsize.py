@@ -129,7 +129,11 @@ def _run_config(losa, cid, taus, later_step=None, n_heads_checked=3, seed=0):
             sq, sk, sv = (synth.perturb_on_device(cfg, x, later_step, i)
                           for i, x in enumerate((tq, tk, tv)))
         so, slse = losa.sparse_attn(sq, sk, sv, idx, cnt, block=blk, want_lse=True)
+        plan = losa.sparse_plan(cnt, block=blk, head_dim=cfg.head_dim)
+        sop, slsep = losa.sparse_attn(sq, sk, sv, idx, cnt, block=blk, want_lse=True, plan=plan)
         torch.cuda.synchronize()
+        assert torch.equal(sop, so) and torch.equal(slsep, slse), (cid, tau, "planned")
+        del sop, slsep
         idx_g, cnt_g = idx.cpu().numpy(), cnt.cpu().numpy()
         so_g, slse_g = so.float().cpu().numpy(), slse.cpu().numpy()
         if later_step is not None:

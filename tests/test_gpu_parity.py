@@ -74,6 +74,18 @@ CASES = {
 }
 
 
+def _check_plan(plan, count, blk):
+    """A plan is a permutation of the work items (one per 128 query rows of
+    each (b, h)) whose costs -- the largest count in the item -- never rise."""
+    b, h, nb = count.shape
+    qpw = 2 if blk == 64 else 1
+    wph = (nb + qpw - 1) // qpw
+    assert np.array_equal(np.sort(plan), np.arange(b * h * wph))
+    flat = count.reshape(b * h, nb)
+    cost = np.array([flat[i // wph, (i % wph) * qpw:(i % wph) * qpw + qpw].max() for i in plan])
+    assert (np.diff(cost) <= 0).all()
+
+
 def _compare_attention(o_gpu, lse_gpu, o_ref, lse_ref, what):
     err = np.abs(o_gpu.astype(np.float64) - o_ref)
     assert err.max() <= O_MAX, f"{what}: max-abs {err.max():.3e}"
@@ -123,7 +135,12 @@ def test_pipeline_matches_oracle(losa, name):
         idx, count = losa.select(mass, tau)
         _say(f"[parity] {name}: sparse tau={tau}")
         os_, lses = losa.sparse_attn(tq, tk, tv, idx, count, block=blk, want_lse=True)
+        # the planned launch (work items longest-first) gives the same bits
+        plan = losa.sparse_plan(count, block=blk)
+        op_, lsep = losa.sparse_attn(tq, tk, tv, idx, count, block=blk, want_lse=True, plan=plan)
         torch.cuda.synchronize()
+        assert torch.equal(op_, os_) and torch.equal(lsep, lses), f"{name} planned tau={tau}"
+        _check_plan(plan.cpu().numpy(), count.cpu().numpy(), blk)
         idx_g, cnt_g, os_g, lses_g = _np(idx), _np(count), _np(os_), _np(lses)
         for b in range(cfg.batch):
             for h in range(cfg.heads):
