@@ -11,9 +11,9 @@
 //    denoising steps (ubos.tech blog, "Key Findings"; aitobox blog, "Key
 //    Highlights"); R measures that on the caller's own inputs;
 //  * sparse_plan_kernel -- a dispatch order for the sparse kernel, made once
-//    per set of frozen lists: the work items sorted by descending cost so
-//    that, dealt round-robin to the XCDs in dispatch order, every XCD gets
-//    the same mix of long and short items and runs its longest ones first.
+//    per set of frozen lists: the work items ranked by descending cost and
+//    dealt to the XCDs so that every XCD gets the same mix of long and short
+//    items and runs its longest ones first (layout below).
 //    Per-head kept fractions range from a few percent to all blocks, and in
 //    the default head-major order the last items to start are often long
 //    ones, leaving the chip part-idle at the end.
@@ -73,44 +73,98 @@ __global__ void __launch_bounds__(256) retained_mass_kernel(const float* __restr
   if (lane == 0) retained[item] = acc / (float)rows;
 }
 
-// One workgroup: a counting sort of the items by cost, descending.  Cost of
-// item (bh, w) = the largest count among query blocks w*qpw .. w*qpw+qpw-1
-// (clamped to [0, nb]); it tracks the item's tile count, the length of the
-// union of those lists.  Items of equal cost land in an unspecified order
-// (LDS atomics), which changes which workgroup runs an item, never its
-// result.
+// Plan layout.  Items are ranked by cost, descending, in kPlanBuckets
+// buckets (cost * kPlanBuckets / (nb + 1)); within a bucket they keep their
+// index order (head-major, query blocks ascending), so runs of consecutive
+// ranks are neighbouring query blocks of one head, whose lists overlap.
+// Runs of kPlanChunk ranks go to one XCD, runs dealt to the 8 XCDs in turn:
+// rank s -> chunk c = s / kPlanChunk, XCD x = c % 8, round r = c / 8, and
+// slot 8 * (r * kPlanChunk + s % kPlanChunk) + x, which the hardware hands
+// to XCD x as its (r * kPlanChunk + s % kPlanChunk)-th workgroup.  Every XCD
+// thus gets the same mix of costs, longest first, and the workgroups
+// resident on an XCD mostly share one head's K/V.  Slots past the last item
+// hold -1.  (On the Wan2.1-1.3B lists this keeps the simulated makespan
+// within 3 % of the balanced bound; sorting by exact cost reaches 1 % but
+// scatters each head's query blocks and doubled the K/V traffic.)
+constexpr int kPlanBuckets = 32;
+constexpr int kPlanChunk = 8;
+
+__host__ __device__ inline long long plan_slots(long long n_items) {
+  const long long chunks = (n_items + kPlanChunk - 1) / kPlanChunk;
+  return (long long)kXcds * kPlanChunk * ((chunks + kXcds - 1) / kXcds);
+}
+
+__device__ __forceinline__ int plan_slot(int s) {
+  const int c = s / kPlanChunk;
+  return kXcds * ((c / kXcds) * kPlanChunk + s % kPlanChunk) + c % kXcds;
+}
+
+// One workgroup of 1024 threads: a stable counting sort of the items by
+// bucket (histogram, then tiles of 1024 items in index order, ranks within a
+// tile from wave ballots), written straight to the slots.  Deterministic.
 __global__ void __launch_bounds__(1024) sparse_plan_kernel(const int32_t* __restrict__ count,
                                                            int nb, int qpw, int n_items, int wph,
                                                            int32_t* __restrict__ order) {
-  __shared__ int hist[1025];
-  const int tid = threadIdx.x;
-  for (int c = tid; c <= nb; c += 1024) hist[c] = 0;
-  __syncthreads();
-  auto cost_of = [&](int item) -> int {
+  __shared__ int start[kPlanBuckets];       // next rank of each bucket
+  __shared__ int wcnt[16][kPlanBuckets];    // per-wave bucket counts of a tile
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  auto bucket_of = [&](int item) -> int {
     const int bh = item / wph;
     const int w = item - bh * wph;
     const int q0 = w * qpw;
     int c = 0;
     for (int q = q0; q < min(nb, q0 + qpw); ++q)
       c = max(c, min(max(count[(size_t)bh * nb + q], 0), nb));
-    return c;
+    return min(kPlanBuckets - 1, c * kPlanBuckets / (nb + 1));
   };
-  for (int item = tid; item < n_items; item += 1024) atomicAdd(&hist[cost_of(item)], 1);
+  if (tid < kPlanBuckets) start[tid] = 0;
   __syncthreads();
-  if (tid == 0) {  // exclusive prefix, highest cost first
+  for (int item = tid; item < n_items; item += 1024) atomicAdd(&start[bucket_of(item)], 1);
+  __syncthreads();
+  if (tid == 0) {  // exclusive prefix, most expensive bucket first
     int run = 0;
-    for (int c = nb; c >= 0; --c) {
-      const int h = hist[c];
-      hist[c] = run;
+    for (int k = kPlanBuckets - 1; k >= 0; --k) {
+      const int h = start[k];
+      start[k] = run;
       run += h;
     }
   }
+  // slots of the last round that no rank reaches
+  const int slots = (int)plan_slots(n_items);
+  for (int j = tid; j < kXcds * kPlanChunk; j += 1024) {
+    const int slot = slots - kXcds * kPlanChunk + j;
+    const int x = slot % kXcds, within = slot / kXcds;
+    const int s_rank = ((within / kPlanChunk) * kXcds + x) * kPlanChunk + within % kPlanChunk;
+    if (s_rank >= n_items) order[slot] = -1;
+  }
   __syncthreads();
-  for (int item = tid; item < n_items; item += 1024) {
-    const int pos = atomicAdd(&hist[cost_of(item)], 1);
-    order[pos] = item;
+  for (int base = 0; base < n_items; base += 1024) {
+    const int item = base + tid;
+    const int bkt = item < n_items ? bucket_of(item) : -1;
+    const unsigned long long below = lane ? ((~0ull) >> (64 - lane)) : 0ull;
+    int rank = 0;
+    for (int k = 0; k < kPlanBuckets; ++k) {
+      const unsigned long long m = __ballot(bkt == k);
+      if (bkt == k) rank = __popcll(m & below);
+      if (lane == 0) wcnt[wave][k] = __popcll(m);
+    }
+    __syncthreads();
+    if (bkt >= 0) {
+      int s_rank = start[bkt] + rank;
+      for (int w2 = 0; w2 < wave; ++w2) s_rank += wcnt[w2][bkt];
+      order[plan_slot(s_rank)] = item;
+    }
+    __syncthreads();
+    if (tid < kPlanBuckets) {
+      int add = 0;
+      for (int w2 = 0; w2 < 16; ++w2) add += wcnt[w2][tid];
+      start[tid] += add;
+    }
+    __syncthreads();
   }
 }
+
+long long sparse_plan_slots(long long n_items) { return plan_slots(n_items); }
 
 hipError_t launch_sparse_plan(const int32_t* count, int32_t nb, int32_t qpw, int32_t bh_count,
                               int32_t* order, hipStream_t stream) {

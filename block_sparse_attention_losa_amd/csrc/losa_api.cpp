@@ -60,6 +60,9 @@ int64_t plan_items(const losa_attn_desc* d, int32_t nb) {
   const int32_t qpw = blocks_per_item(d);
   return int64_t{d->batch} * d->heads * ((nb + qpw - 1) / qpw);
 }
+int64_t plan_entries(const losa_attn_desc* d, int32_t nb) {
+  return losa::sparse_plan_slots(plan_items(d, nb));
+}
 
 }  // namespace
 
@@ -237,7 +240,7 @@ losa_status losa_sparse_attn(const losa_attn_desc* desc, const void* q, const vo
 int64_t losa_sparse_plan_size(const losa_attn_desc* desc) {
   int32_t nb = 0;
   if (check_desc(desc, &nb) != LOSA_OK) return -1;
-  return 4 * plan_items(desc, nb);
+  return 4 * plan_entries(desc, nb);
 }
 
 losa_status losa_sparse_plan(const losa_attn_desc* desc, const int32_t* count, int32_t* plan,
@@ -247,7 +250,7 @@ losa_status losa_sparse_plan(const losa_attn_desc* desc, const int32_t* count, i
   if (st != LOSA_OK) return st;
   if (!count || !plan) return LOSA_ERR_NULL_POINTER;
   if (!aligned(count, 4) || !aligned(plan, 4)) return LOSA_ERR_MISALIGNED;
-  if (plan_bytes < 4 * plan_items(desc, nb)) return LOSA_ERR_WORKSPACE;
+  if (plan_bytes < 4 * plan_entries(desc, nb)) return LOSA_ERR_WORKSPACE;
   return device_status(losa::launch_sparse_plan(count, nb, blocks_per_item(desc),
                                                 desc->batch * desc->heads, plan,
                                                 static_cast<hipStream_t>(stream)));

@@ -50,8 +50,10 @@ hipError_t launch_select(int32_t rows, int32_t nkb, const float* mass, double ta
                          hipStream_t stream);
 
 // Dispatch order for the sparse kernel: the work items (bh * wph + w, one per
-// group of qpw query blocks) sorted by descending cost, cost = the largest
-// count among the group's query blocks.  order: [bh_count * wph] int32.
+// group of qpw query blocks) ranked by descending cost, cost = the largest
+// count among the group's query blocks, laid out per XCD (frozen_lists.hip).
+// order: [sparse_plan_slots(bh_count * wph)] int32, -1 in unused slots.
+long long sparse_plan_slots(long long n_items);
 hipError_t launch_sparse_plan(const int32_t* count, int32_t nb, int32_t qpw, int32_t bh_count,
                               int32_t* order, hipStream_t stream);
 

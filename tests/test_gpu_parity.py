@@ -75,15 +75,28 @@ CASES = {
 
 
 def _check_plan(plan, count, blk):
-    """A plan is a permutation of the work items (one per 128 query rows of
-    each (b, h)) whose costs -- the largest count in the item -- never rise."""
+    """A plan places every work item (one per 128 query rows of each (b, h))
+    exactly once; read in rank order (runs of 8 ranks per XCD, dealt to the 8
+    XCDs in turn), the cost buckets never rise and items of one bucket keep
+    their index order.  Unused slots hold -1."""
     b, h, nb = count.shape
     qpw = 2 if blk == 64 else 1
     wph = (nb + qpw - 1) // qpw
-    assert np.array_equal(np.sort(plan), np.arange(b * h * wph))
+    n = b * h * wph
+    assert np.array_equal(np.sort(plan[plan >= 0]), np.arange(n))
+    assert (plan[plan < 0] == -1).all()
+    ch, xcds = 8, 8
+    slots = np.arange(len(plan))
+    x, within = slots % xcds, slots // xcds
+    rank = ((within // ch) * xcds + x) * ch + within % ch
+    items = plan[np.argsort(rank)]
+    items = items[items >= 0]
     flat = count.reshape(b * h, nb)
-    cost = np.array([flat[i // wph, (i % wph) * qpw:(i % wph) * qpw + qpw].max() for i in plan])
-    assert (np.diff(cost) <= 0).all()
+    cost = np.array([flat[i // wph, (i % wph) * qpw:(i % wph) * qpw + qpw].max() for i in items])
+    bucket = np.minimum(31, cost * 32 // (nb + 1))
+    assert (np.diff(bucket) <= 0).all()
+    same = np.diff(bucket) == 0
+    assert (np.diff(items)[same] > 0).all()
 
 
 def _compare_attention(o_gpu, lse_gpu, o_ref, lse_ref, what):
