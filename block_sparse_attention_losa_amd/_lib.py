@@ -46,6 +46,12 @@ class AttnDesc(ctypes.Structure):
         ("block", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
+        ("stride_batch", ctypes.c_int64),
+        ("stride_head", ctypes.c_int64),
+        ("stride_token", ctypes.c_int64),
+        ("o_stride_batch", ctypes.c_int64),
+        ("o_stride_head", ctypes.c_int64),
+        ("o_stride_token", ctypes.c_int64),
     ]
 
 

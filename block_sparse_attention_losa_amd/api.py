@@ -19,14 +19,32 @@ def num_blocks(seq_len: int, block: int) -> int:
     return (int(seq_len) + int(block) - 1) // int(block)
 
 
-def make_desc(q: torch.Tensor, block: int, scale=None) -> _lib.AttnDesc:
+def _layout(t):
+    """Element strides (batch, head, token) of a [B, H, N, D]-shaped tensor,
+    or zeros when it is contiguous.  Non-contiguous views (e.g. a
+    [B, N, H, D] tensor permuted to [B, H, N, D], or one of q/k/v of a packed
+    projection) need a contiguous head dim and bfloat16."""
+    if t is None or t.is_contiguous():
+        return (0, 0, 0)
+    if t.stride(-1) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    if t.dtype != torch.bfloat16:
+        raise TypeError("strided layouts are supported for bfloat16 only")
+    return (t.stride(0), t.stride(1), t.stride(2))
+
+
+def make_desc(q: torch.Tensor, block: int, scale=None, k=None, v=None, o=None) -> _lib.AttnDesc:
     if q.dim() != 4:
         raise ValueError("expected [B, H, N, D] tensors")
     if q.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {q.dtype}")
     b, h, n, d = q.shape
+    lay = _layout(q)
+    for t in (k, v):
+        if t is not None and _layout(t) != lay:
+            raise ValueError("q, k and v must share one memory layout")
     return _lib.AttnDesc(b, h, n, d, int(block), _DTYPES[q.dtype],
-                         0.0 if scale is None else float(scale))
+                         0.0 if scale is None else float(scale), *lay, *_layout(o))
 
 
 def _ptr(t):
@@ -37,25 +55,31 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _check_inputs(*ts):
-    ref = ts[0]
-    for t in ts:
+def _check_inputs(*ts, strided=()):
+    """Device checks; tensors in ``strided`` may be non-contiguous views
+    (their layout goes to the descriptor), the others must be contiguous."""
+    present = [t for t in tuple(strided) + tuple(ts) if t is not None]
+    for t in present:
         if not t.is_cuda:
             raise ValueError("tensors must live on a GPU")
-        if t.device != ref.device:
+        if t.device != present[0].device:
             raise ValueError("tensors must share one device")
-        if not t.is_contiguous():
+    for t in ts:
+        if t is not None and not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
 
 
 def dense_attn(q, k, v, block: int = 64, scale=None, o=None, lse=None, want_lse=True):
-    """Dense softmax attention; returns ``(o, lse)`` (lse None if not wanted)."""
-    _check_inputs(q, k, v)
+    """Dense softmax attention; returns ``(o, lse)`` (lse None if not wanted).
+    q, k, v (and o) are [B, H, N, D]; bfloat16 views with other strides (a
+    permuted [B, N, H, D] tensor, slices of a packed projection) are read
+    and written in place."""
+    _check_inputs(lse, strided=(q, k, v, o))
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share shape and dtype")
-    desc = make_desc(q, block, scale)
     if o is None:
-        o = torch.empty_like(q)
+        o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    desc = make_desc(q, block, scale, k, v, o)
     if lse is None and want_lse:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     lib = _lib.load()
@@ -67,10 +91,10 @@ def dense_attn(q, k, v, block: int = 64, scale=None, o=None, lse=None, want_lse=
 def block_mass(q, k, block: int = 64, lse=None, scale=None, mass=None, lse_scratch=None):
     """Block mass map ``[B, H, nb, nb]`` (float32); runs the lse pass first
     when ``lse`` is None."""
-    _check_inputs(q, k)
+    _check_inputs(mass, lse, lse_scratch, strided=(q, k))
     if k.shape != q.shape or k.dtype != q.dtype:
         raise ValueError("q, k must share shape and dtype")
-    desc = make_desc(q, block, scale)
+    desc = make_desc(q, block, scale, k)
     b, h, n, _ = q.shape
     nb = num_blocks(n, block)
     if mass is None:
@@ -97,14 +121,14 @@ def dense_attn_mass(q, k, v, block: int = 64, scale=None, o=None, lse=None, mass
     of the same inputs.  Returns ``(o, lse, mass)``.  ``workspace`` is a
     uint8 device tensor of at least :func:`dense_attn_mass_workspace_bytes`
     bytes (allocated here when None)."""
-    _check_inputs(q, k, v)
+    _check_inputs(lse, mass, workspace, strided=(q, k, v, o))
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share shape and dtype")
-    desc = make_desc(q, block, scale)
     b, h, n, _ = q.shape
     nb = num_blocks(n, block)
     if o is None:
-        o = torch.empty_like(q)
+        o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    desc = make_desc(q, block, scale, k, v, o)
     if lse is None and want_lse:
         lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
     if mass is None:
@@ -224,7 +248,7 @@ def sparse_attn(q, k, v, idx, count, block: int = 64, scale=None, o=None, lse=No
     """Block-sparse attention over frozen lists; returns ``(o, lse)``.  With
     ``plan`` (from :func:`sparse_plan` on the same counts) the work runs in
     the plan's order; the results are the same."""
-    _check_inputs(q, k, v, idx, count)
+    _check_inputs(idx, count, lse, plan, strided=(q, k, v, o))
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share shape and dtype")
     b, h, n, _ = q.shape
@@ -233,14 +257,13 @@ def sparse_attn(q, k, v, idx, count, block: int = 64, scale=None, o=None, lse=No
         raise ValueError("idx must be [B,H,nb,nb] and count [B,H,nb]")
     if idx.dtype != torch.int32 or count.dtype != torch.int32:
         raise TypeError("idx and count must be int32")
-    desc = make_desc(q, block, scale)
     if o is None:
-        o = torch.empty_like(q)
+        o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    desc = make_desc(q, block, scale, k, v, o)
     if lse is None and want_lse:
         lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
     lib = _lib.load()
     if plan is not None:
-        _check_inputs(q, plan)
         if plan.dtype != torch.int32:
             raise TypeError("plan must be int32")
         _lib.check("losa_sparse_attn_planned", lib.losa_sparse_attn_planned(

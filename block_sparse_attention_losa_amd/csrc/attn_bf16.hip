@@ -176,7 +176,9 @@ __global__ void __launch_bounds__(256, (D == 64 ? 3 : 2)) attn_bf16_kernel(AttnP
   if (item < 0 || item >= wph * bh_count) return;
   const int bh = item / wph;
   const int w = item - bh * wph;
-  const size_t head_off = (size_t)bh * (size_t)N * D;
+  const size_t head_off =
+      (size_t)(bh / p.heads) * p.stride_b + (size_t)(bh % p.heads) * p.stride_h;
+  const int row_stride = (int)p.stride_n * 2;  // bytes between tokens (fits: checked on the host)
   const bf16* __restrict__ qh = (const bf16*)p.q + head_off;
   const bf16* __restrict__ kh = (const bf16*)p.k + head_off;
   const bf16* __restrict__ vh = (const bf16*)p.v + head_off;
@@ -223,10 +225,11 @@ __global__ void __launch_bounds__(256, (D == 64 ? 3 : 2)) attn_bf16_kernel(AttnP
   // ---- Q^T as the B operand, in registers
   bf16x8 qreg[D / 16];
   {
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qh, N * G::kRowBytes);
+    // rows past N lie beyond the range and read as zero
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qh, (N - 1) * row_stride + G::kRowBytes);
 #pragma unroll
     for (int dk = 0; dk < D / 16; ++dk)
-      qreg[dk] = __builtin_bit_cast(bf16x8, buf_load16(qr, row * G::kRowBytes + dk * 32 + g * 16));
+      qreg[dk] = __builtin_bit_cast(bf16x8, buf_load16(qr, row * row_stride + dk * 32 + g * 16));
   }
 
   // ---- LDS ring: K tiles at slots 0/1, V tiles at slots 2/3
@@ -240,13 +243,13 @@ __global__ void __launch_bounds__(256, (D == 64 ? 3 : 2)) attn_bf16_kernel(AttnP
     const int b = wave * G::kBlocksPerWave + j;
     const int r = b * G::kRowsPerBlock + lane / G::kChunksPerRow;
     const int pc = lane % G::kChunksPerRow;
-    koff[j] = r * G::kRowBytes + swz_k<D>(r, pc) * 16;
-    voff[j] = r * G::kRowBytes + swz_v<D>(r, pc) * 16;
+    koff[j] = r * row_stride + swz_k<D>(r, pc) * 16;
+    voff[j] = r * row_stride + swz_v<D>(r, pc) * 16;
   }
   auto dma_tile = [&](const bf16* src, int key0, unsigned char* slot, const int* off) {
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc((const unsigned char*)src + (size_t)key0 * G::kRowBytes,
-                  (N - key0) * G::kRowBytes);
+        make_rsrc((const unsigned char*)src + (size_t)key0 * row_stride,
+                  (N - key0 - 1) * row_stride + G::kRowBytes);
     // wave-uniform LDS destination (M0 must come from a scalar register)
     const unsigned base =
         __builtin_amdgcn_readfirstlane(lds_addr_of(slot) + wave * G::kBlocksPerWave * 1024);
@@ -514,7 +517,8 @@ __global__ void __launch_bounds__(256, (D == 64 ? 3 : 2)) attn_bf16_kernel(AttnP
     }
     if constexpr (G::kWithV) {
       const float inv = empty ? 0.f : 1.0f / l_tot;
-      bf16* orow = (bf16*)p.o + head_off + (size_t)row * D;
+      bf16* orow = (bf16*)p.o + (size_t)(bh / p.heads) * p.o_stride_b +
+                   (size_t)(bh % p.heads) * p.o_stride_h + (size_t)row * p.o_stride_n;
 #pragma unroll
       for (int mt = 0; mt < kORegs; ++mt)
 #pragma unroll

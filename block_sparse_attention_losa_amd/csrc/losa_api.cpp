@@ -23,6 +23,19 @@ losa_status check_desc(const losa_attn_desc* d, int32_t* nb_out) {
   const int64_t items = static_cast<int64_t>(d->batch) * d->heads * nb;
   if (items >= (int64_t{1} << 31)) return LOSA_ERR_BAD_SHAPE;
   if (!std::isfinite(d->scale) || d->scale < 0.f) return LOSA_ERR_BAD_ARGUMENT;
+  if (static_cast<int64_t>(d->seq_len) * d->head_dim * 2 >= (int64_t{1} << 31))
+    return LOSA_ERR_BAD_SHAPE;
+  for (int t = 0; t < 2; ++t) {
+    const int64_t sb = t ? d->o_stride_batch : d->stride_batch;
+    const int64_t sh = t ? d->o_stride_head : d->stride_head;
+    const int64_t sn = t ? d->o_stride_token : d->stride_token;
+    if (sb == 0 && sh == 0 && sn == 0) continue;  // contiguous
+    if (d->dtype != LOSA_BF16) return LOSA_ERR_BAD_ARGUMENT;
+    if (sn < d->head_dim || sh < 0 || sb < 0) return LOSA_ERR_BAD_ARGUMENT;
+    if (sn % 8 || sh % 8 || sb % 8) return LOSA_ERR_MISALIGNED;
+    if ((static_cast<int64_t>(d->seq_len) - 1) * sn * 2 + 2 * d->head_dim >= (int64_t{1} << 31))
+      return LOSA_ERR_BAD_SHAPE;
+  }
   *nb_out = static_cast<int32_t>(nb);
   return LOSA_OK;
 }
@@ -37,6 +50,17 @@ losa::AttnParams base_params(const losa_attn_desc* d, int32_t nb) {
   p.nb = nb;
   p.items = d->batch * d->heads * nb;
   p.scale = effective_scale(d);
+  p.heads = d->heads;
+  const long long cn = d->head_dim, ch = static_cast<long long>(d->seq_len) * d->head_dim,
+                  cb = ch * d->heads;  // contiguous [B, H, N, D]
+  const bool in_c = d->stride_batch == 0 && d->stride_head == 0 && d->stride_token == 0;
+  const bool out_c = d->o_stride_batch == 0 && d->o_stride_head == 0 && d->o_stride_token == 0;
+  p.stride_b = in_c ? cb : d->stride_batch;
+  p.stride_h = in_c ? ch : d->stride_head;
+  p.stride_n = in_c ? cn : d->stride_token;
+  p.o_stride_b = out_c ? cb : d->o_stride_batch;
+  p.o_stride_h = out_c ? ch : d->o_stride_head;
+  p.o_stride_n = out_c ? cn : d->o_stride_token;
   return p;
 }
 

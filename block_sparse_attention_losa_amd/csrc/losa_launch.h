@@ -23,6 +23,11 @@ struct AttnParams {
   float* rowsum;         // dense+mass: [B*H, nb, N] log2 block sums (workspace)
   float* rowref;         // dense+mass: [B*H, N] per-row offsets (workspace)
   const int32_t* order;  // sparse: workgroup b runs work item order[b] (a plan), or null
+  // element strides (batch, head, token; the head dim is contiguous) of Q, K
+  // and V, and of O: D*N*H, D*N, D for [B,H,N,D]; D*H*N, D, D*H for [B,N,H,D]
+  long long stride_b, stride_h, stride_n;
+  long long o_stride_b, o_stride_h, o_stride_n;
+  int32_t heads;         // H (to split the (batch, head) index)
   int32_t n;             // tokens
   int32_t nb;            // blocks per sequence
   int32_t items;         // B*H*nb work items (one per query block)

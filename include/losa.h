@@ -12,9 +12,10 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  - Tensors Q, K, V, O are contiguous [B, H, N, D] (D fastest) in device
- *    memory, element type bf16 or fp32 (losa_dtype); they must be 16-byte
- *    aligned.  lse is [B, H, N] fp32, natural log.  mass is [B, H, nb, nb]
+ *  - Tensors Q, K, V, O are [B, H, N, D] (D fastest) in device memory,
+ *    element type bf16 or fp32 (losa_dtype), 16-byte aligned: contiguous by
+ *    default, or (bf16) laid out by the strides in losa_attn_desc, e.g. the
+ *    [B, N, H, D] layout a DiT projection produces, read in place.  lse is [B, H, N] fp32, natural log.  mass is [B, H, nb, nb]
  *    fp32 (key block fastest); idx is [B, H, nb, nb] int32 and count
  *    [B, H, nb] int32.  nb = ceil(N / block); the last block holds the
  *    N - (nb-1)*block remaining tokens.  fp32/int32 arrays must be 4-byte
@@ -66,6 +67,20 @@ typedef struct {
   int32_t block;     /* square block size (query and key), 64 or 128      */
   int32_t dtype;     /* losa_dtype of Q, K, V and O                        */
   float scale;       /* softmax scale c; 0 selects 1/sqrt(D)              */
+  /* Element strides between batch items, heads and tokens (the D elements of
+   * a token are contiguous) of Q, K and V (shared) and of O.  A triple of 0s
+   * means contiguous [B, H, N, D].  Otherwise (bf16 only): token stride >= D,
+   * every stride a multiple of 8 elements (16 bytes) and >= 0, and
+   * (N-1)*token_stride*2 + 2*D < 2^31.  Examples: [B, N, H, D] is
+   * (N*H*D, D, H*D); Q of a packed [B, N, 3, H, D] projection is
+   * (3*N*H*D, D, 3*H*D).  lse, mass, idx and count stay contiguous.  The O
+   * layout must not make two output elements alias. */
+  int64_t stride_batch;
+  int64_t stride_head;
+  int64_t stride_token;
+  int64_t o_stride_batch;
+  int64_t o_stride_head;
+  int64_t o_stride_token;
 } losa_attn_desc;
 
 /* ceil(seq_len / block), or -1 when desc is NULL or block < 1. */

@@ -74,6 +74,22 @@ def test_descriptor_validation(lib, kw, code):
     assert lib.losa_dense_attn_mass_workspace(d) == -1
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(stride_token=64), 7),                                  # token stride < D
+    (dict(stride_batch=8, stride_head=8), 7),                    # token stride missing
+    (dict(stride_batch=16 * 128 * 1000, stride_head=128, stride_token=2 * 128 + 4), 5),
+    (dict(stride_batch=16 * 128 * 1000, stride_head=132, stride_token=2 * 128), 5),
+    (dict(dtype=1, stride_batch=2 * 128 * 1000, stride_head=128, stride_token=2 * 128), 7),
+    (dict(o_stride_token=100), 7),
+    (dict(o_stride_batch=-8, o_stride_head=128, o_stride_token=256), 7),
+    (dict(seq_len=60000, stride_batch=8, stride_head=8, stride_token=8 * 4096), 2),
+])
+def test_layout_validation(lib, kw, code):
+    d = desc(**kw)
+    assert lib.losa_dense_attn(d, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == code
+    assert lib.losa_sparse_attn(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == code
+
+
 def test_null_and_alignment(lib):
     d = desc()
     assert lib.losa_dense_attn(None, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == 1
