@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_wan13_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_attention_losa_amd", "csrc", f)
-                  for f in ("attn_bf16.hip", "losa_device.h")]
+                  for f in ("attn_bf16.hip", "attn_common.h", "losa_device.h")]
 
 
 def log(msg):
