@@ -18,7 +18,10 @@
 // the K/V feed alone would need the whole L2 bandwidth at MFMA peak.  For
 // sparse attention the workgroup walks the union of its query blocks' frozen
 // lists (ascending) and each wave skips the tiles its own block did not
-// keep.
+// keep.  Workgroups take their work item from the XCD-aware default order
+// or, for sparse attention, from a launch plan (frozen_lists.hip) that runs
+// the items longest-first and evenly over the XCDs.  Q, K, V and O may use
+// any bf16 layout with a contiguous head dim (per-tensor element strides).
 //
 // Data movement is CDNA4-native:
 //  * K and V tiles go from HBM straight into LDS with buffer loads in LDS
@@ -30,7 +33,9 @@
 //    dim) are free of bank conflicts;
 //  * K runs one tile ahead of V: the scores of tile t+1 are computed on the
 //    matrix cores while tile t's softmax runs on the VALU, and the loads of
-//    K(t+2) and V(t+1) are in flight during both.
+//    K(t+2) and V(t+1) are in flight during both; the score MFMAs issue at a
+//    lower wave priority than the softmax, so the two waves of a SIMD tend
+//    to alternate between the matrix core and the VALU.
 //
 // Scores are computed transposed, S^T = K Q^T, on 32x32x16 MFMA tiles: a
 // lane then holds one query row and 16 of the 32 keys of a chunk, so row
