@@ -49,18 +49,20 @@
 
 namespace losa {
 
-template <int D, int BLK, int MODE>
+template <int D, int BLK, int MODE, int ROWS>
 struct GeoB {
   static constexpr bool kWithV = (MODE == kDense || MODE == kSparse || MODE == kDenseMass);
-  static constexpr int kRows = 128;             // query rows per workgroup
+  static constexpr int kRows = ROWS;            // query rows per workgroup (128 or 256)
+  static constexpr int kWaves = ROWS / 32;      // one wave per 32 rows
+  static constexpr int kThreads = 64 * kWaves;
   static constexpr int kQPW = kRows / BLK;      // query blocks per workgroup
-  static constexpr int kWavesPerBlock = 4 / kQPW;
+  static constexpr int kWavesPerBlock = kWaves / kQPW;
   static constexpr int kSubs = BLK / 64;        // 64-key tiles per key block
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kTileBytes = 64 * kRowBytes;
   static constexpr int kChunksPerRow = kRowBytes / 16;
   static constexpr int kBlocksPerTile = kTileBytes / 1024;  // 1 KB per wave-wide load
-  static constexpr int kBlocksPerWave = kBlocksPerTile / 4;
+  static constexpr int kBlocksPerWave = kBlocksPerTile / kWaves;
   static constexpr int kRowsPerBlock = 1024 / kRowBytes;
   static constexpr int kMaxBlocks = 1024;
   static constexpr int kRingBytes = (kWithV ? 4 : 2) * kTileBytes;  // 2 K + 2 V tiles
@@ -73,9 +75,11 @@ struct GeoB {
 // loop is bound by the softmax VALU work rather than the matrix cores, and a
 // third wave per SIMD (168 VGPRs, a few spilled values reloaded per step)
 // hides more of its latency: measured 3-4 % faster than two waves.
-template <int D, int BLK, int MODE>
-__global__ void __launch_bounds__(256, (D == 64 ? 3 : 2)) attn_bf16_kernel(AttnParams p) {
-  using G = GeoB<D, BLK, MODE>;
+template <int D, int BLK, int MODE, int ROWS>
+__global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 2)))
+    attn_bf16_kernel(AttnParams p) {
+  using G = GeoB<D, BLK, MODE, ROWS>;
+  static_assert(ROWS == 128 || MODE == kDense || MODE == kDenseMass, "256 rows: dense passes");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   const int nb = p.nb, N = p.n;
@@ -111,8 +115,8 @@ __global__ void __launch_bounds__(256, (D == 64 ? 3 : 2)) attn_bf16_kernel(AttnP
     int* lst = flag + G::kMaxBlocks;
     int* ccount = lst + G::kMaxBlocks;
     const int qb0 = w * G::kQPW;
-    nblk = build_union_list<G::kQPW>(p.idx, p.cnt, (size_t)bh * nb + qb0,
-                                     min(G::kQPW, nb - qb0), nb, flag, lst, ccount);
+    nblk = build_union_list<G::kQPW, G::kThreads>(p.idx, p.cnt, (size_t)bh * nb + qb0,
+                                                  min(G::kQPW, nb - qb0), nb, flag, lst, ccount);
     list = lst;
   }
   float* part = nullptr;  // kMass: per-wave partial tile sums [4][nb]
@@ -446,10 +450,10 @@ __global__ void __launch_bounds__(256, (D == 64 ? 3 : 2)) attn_bf16_kernel(AttnP
   }
 }
 
-template <int D, int BLK, int MODE>
+template <int D, int BLK, int MODE, int ROWS = 128>
 hipError_t launch_b(const AttnParams& p, hipStream_t stream) {
-  using G = GeoB<D, BLK, MODE>;
-  auto kern = attn_bf16_kernel<D, BLK, MODE>;
+  using G = GeoB<D, BLK, MODE, ROWS>;
+  auto kern = attn_bf16_kernel<D, BLK, MODE, ROWS>;
   static hipError_t attr = hipFuncSetAttribute((const void*)kern,
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                G::kLdsBytes);
@@ -457,18 +461,18 @@ hipError_t launch_b(const AttnParams& p, hipStream_t stream) {
   const int wph = (p.nb + G::kQPW - 1) / G::kQPW;
   const int grid = p.order != nullptr ? (int)sparse_plan_slots((long long)wph * (p.items / p.nb))
                                        : xcd_grid(wph, p.items / p.nb);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), G::kLdsBytes, stream, p);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(G::kThreads), G::kLdsBytes, stream, p);
   return hipGetLastError();
 }
 
 template <int D, int BLK>
 hipError_t launch_b_mode(int mode, const AttnParams& p, hipStream_t stream) {
   switch (mode) {
-    case kDense: return launch_b<D, BLK, kDense>(p, stream);
-    case kSparse: return launch_b<D, BLK, kSparse>(p, stream);
+    case kDense: return launch_b<D, BLK, kDense, attn_rows(kDense, D, BLK)>(p, stream);
+    case kSparse: return launch_b<D, BLK, kSparse, attn_rows(kSparse, D, BLK)>(p, stream);
     case kLse: return launch_b<D, BLK, kLse>(p, stream);
     case kMass: return launch_b<D, BLK, kMass>(p, stream);
-    case kDenseMass: return launch_b<D, BLK, kDenseMass>(p, stream);
+    case kDenseMass: return launch_b<D, BLK, kDenseMass, attn_rows(kDenseMass, D, BLK)>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

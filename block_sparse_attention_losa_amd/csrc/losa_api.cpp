@@ -77,9 +77,11 @@ int64_t dense_mass_workspace(const losa_attn_desc* d, int32_t nb) {
   return rowsum_bytes(d, nb) + int64_t{4} * d->batch * d->heads * d->seq_len;
 }
 
-// Sparse work items: one per 128 query rows of each (b, h), i.e. per pair of
-// 64-token query blocks or per 128-token block.
-int32_t blocks_per_item(const losa_attn_desc* d) { return d->block == 64 ? 2 : 1; }
+// Sparse work items: one per workgroup of the sparse kernel, i.e. per
+// losa::attn_rows query rows of each (b, h).
+int32_t blocks_per_item(const losa_attn_desc* d) {
+  return losa::attn_rows(losa::kSparse, d->head_dim, d->block) / d->block;
+}
 int64_t plan_items(const losa_attn_desc* d, int32_t nb) {
   const int32_t qpw = blocks_per_item(d);
   return int64_t{d->batch} * d->heads * ((nb + qpw - 1) / qpw);
