@@ -113,6 +113,97 @@ def cpu_baseline(cfg, q, k, v, idx, count, budget_s):
                       f"on the step-4 input, {dt:.1f} s, scaled to the full call"}
 
 
+def host_info():
+    """Host facts the oracle timings depend on: BLAS threads, CPU model and
+    numpy's BLAS."""
+    import numpy as np
+
+    threads, blas = os.cpu_count() or 1, "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            threads = max(i.get("num_threads", 1) for i in info)
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+    except Exception:  # pragma: no cover - informational only
+        pass
+    if blas == "unknown":
+        try:
+            cfg = np.show_config(mode="dicts")
+            blas = cfg["Build Dependencies"]["blas"]["name"]
+        except Exception:  # pragma: no cover - informational only
+            pass
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover - informational only
+        pass
+    return {"cores": int(threads), "cpu_model": model, "blas": blas,
+            "affinity": len(os.sched_getaffinity(0))}
+
+
+def oracle_profile(cfg, step3, later, mass, idx, count, tau, budget_s):
+    """Each oracle function of the path on a bounded random sample of its
+    work (query blocks of random heads; rows of the mass map for the
+    selection), scaled to seconds per full call on the workload: the dense
+    pass, the mass map and the selection on the construction-step inputs
+    ``step3``, sparse attention on a later-step input ``later``."""
+    import numpy as np
+
+    import oracle
+
+    nb, blk = cfg.num_blocks, cfg.block
+    rng = np.random.default_rng(1)
+    bh = [(bb, hh) for bb in range(cfg.batch) for hh in range(cfg.heads)]
+    units = len(bh) * nb
+
+    def sample(fn):
+        done, t0 = 0, time.perf_counter()
+        for j in rng.permutation(units):
+            (bb, hh), i = bh[j // nb], int(j % nb)
+            fn(bb, hh, i)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return {"s_per_call": round(dt / done * units, 2),
+                "sample": f"{done} of {units} query blocks, {dt:.1f} s"}
+
+    def rows_of(i):
+        lo, hi = oracle.block_rows(i, cfg.seq_len, blk)
+        return np.arange(lo, hi)
+
+    def mass_of_block(bb, hh, i):
+        # both passes for one query block: its rows' lse, then its mass row
+        rows = rows_of(i)
+        lse = np.zeros(cfg.seq_len)
+        lse[rows] = oracle.row_lse(q[bb, hh], k[bb, hh], rows=rows)
+        return oracle.block_mass(q[bb, hh], k[bb, hh], blk, lse=lse, qblocks=[i])
+
+    (q, k, v), (q4, k4, v4) = step3, later
+    res = {"dense_attention": sample(lambda bb, hh, i: oracle.dense_attention(
+               q[bb, hh], k[bb, hh], v[bb, hh], rows=rows_of(i))),
+           "block_mass": sample(lambda bb, hh, i: mass_of_block(bb, hh, i)),
+           "sparse_attention": sample(lambda bb, hh, i: oracle.sparse_attention(
+               q4[bb, hh], k4[bb, hh], v4[bb, hh], idx[bb, hh], count[bb, hh], blk,
+               qblocks=[i]))}
+    rows = mass.reshape(-1, nb)
+    pick = rng.permutation(rows.shape[0])
+    done, t0 = 0, time.perf_counter()
+    while done < len(pick) and time.perf_counter() - t0 <= budget_s:
+        oracle.select(rows[pick[done:done + 64]], tau)
+        done += min(64, len(pick) - done)
+    dt = time.perf_counter() - t0
+    res["select"] = {"s_per_call": round(dt / done * rows.shape[0], 2),
+                     "sample": f"{done} of {rows.shape[0]} rows, {dt:.1f} s"}
+    res.update(host_info())
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +216,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--oracle-profile", type=float, default=0.0, metavar="SECONDS",
+                    help="also time every oracle function on a sample of about this many "
+                         "seconds each (off by default)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -279,6 +373,11 @@ def main():
     dflops = dense_flops(b, h, n, d)
     dense_mean = float(np.mean(dense_later_ms)) if dense_later_ms else None
     traffic = read_traffic(1)
+    # the selection is HBM-bound: it reads the mass map and writes the lists
+    rows = b * h * nb
+    select_bytes = 4 * nb * rows + 4 * int(cnt_h.sum()) + 4 * rows
+    select_mean = float(np.mean(select_ms))
+    props = torch.cuda.get_device_properties(dev)
 
     out = {
         "metric": METRIC,
@@ -316,6 +415,12 @@ def main():
                             "two_pass_block_mass": round(float(np.mean(two_mass_ms)), 4),
                             "max_mass_gap_one_sweep_vs_two_pass": mass_gap},
         "retained_mass": drift,
+        "select": {"ms": round(select_mean, 4), "algorithmic_mb": round(select_bytes / 1e6, 2),
+                   "gbps": round(select_bytes / (select_mean * 1e-3) / 1e9, 1),
+                   "hbm_peak_gbps": PEAK_HBM_GBS},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "compute_units": props.multi_processor_count,
+                   "memory_gib": round(props.total_memory / 2**30, 1)},
         "kernel_sha": kernel_hash(),
     }
     if not args.no_cpu_baseline:
@@ -324,6 +429,11 @@ def main():
         out["cpu_baseline"] = cpu_baseline(cfg, q4, k4, v4, idx_h, cnt_h, args.cpu_budget)
     else:
         out["cpu_baseline"] = None
+    if args.oracle_profile > 0:
+        log(f"[bench] oracle profile (~{4 * args.oracle_profile:.0f} s)")
+        step4 = tuple(x.float().cpu().numpy() for x in later[0])
+        out["oracle_profile"] = oracle_profile(cfg, (q3, k3, v3), step4, mass.cpu().numpy(),
+                                               idx_h, cnt_h, tau, args.oracle_profile)
     print(json.dumps(out), flush=True)
 
 
