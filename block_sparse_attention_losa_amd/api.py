@@ -69,6 +69,18 @@ def _check_inputs(*ts, strided=()):
             raise ValueError("tensors must be contiguous")
 
 
+def _check_out(t, shape, dtype, name):
+    """A caller-supplied output must have the exact shape and dtype the
+    kernel writes: the C entry points take raw pointers and cannot see a
+    short buffer."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
 def dense_attn(q, k, v, block: int = 64, scale=None, o=None, lse=None, want_lse=True):
     """Dense softmax attention; returns ``(o, lse)`` (lse None if not wanted).
     q, k, v (and o) are [B, H, N, D]; bfloat16 views with other strides (a
@@ -77,6 +89,8 @@ def dense_attn(q, k, v, block: int = 64, scale=None, o=None, lse=None, want_lse=
     _check_inputs(lse, strided=(q, k, v, o))
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share shape and dtype")
+    _check_out(o, q.shape, q.dtype, "o")
+    _check_out(lse, q.shape[:3], torch.float32, "lse")
     if o is None:
         o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     desc = make_desc(q, block, scale, k, v, o)
@@ -97,6 +111,9 @@ def block_mass(q, k, block: int = 64, lse=None, scale=None, mass=None, lse_scrat
     desc = make_desc(q, block, scale, k)
     b, h, n, _ = q.shape
     nb = num_blocks(n, block)
+    _check_out(mass, (b, h, nb, nb), torch.float32, "mass")
+    _check_out(lse, (b, h, n), torch.float32, "lse")
+    _check_out(lse_scratch, (b, h, n), torch.float32, "lse_scratch")
     if mass is None:
         mass = torch.empty((b, h, nb, nb), dtype=torch.float32, device=q.device)
     if lse is None and lse_scratch is None:
@@ -126,6 +143,11 @@ def dense_attn_mass(q, k, v, block: int = 64, scale=None, o=None, lse=None, mass
         raise ValueError("q, k, v must share shape and dtype")
     b, h, n, _ = q.shape
     nb = num_blocks(n, block)
+    _check_out(o, q.shape, q.dtype, "o")
+    _check_out(lse, (b, h, n), torch.float32, "lse")
+    _check_out(mass, (b, h, nb, nb), torch.float32, "mass")
+    if workspace is not None and workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor")
     if o is None:
         o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     desc = make_desc(q, block, scale, k, v, o)
@@ -147,11 +169,13 @@ def select(mass, threshold: float = 0.99, idx=None, count=None):
     """Threshold selection over the last axis of ``mass``; returns
     ``(idx, count)`` with idx shaped like mass (int32; entries at and past
     count are left as allocated) and count shaped ``mass.shape[:-1]``."""
-    _check_inputs(mass)
+    _check_inputs(mass, idx, count)
     if mass.dtype != torch.float32:
         raise TypeError("mass must be float32")
     nkb = mass.shape[-1]
     rows = mass.numel() // nkb if nkb else 0
+    _check_out(idx, mass.shape, torch.int32, "idx")
+    _check_out(count, mass.shape[:-1], torch.int32, "count")
     if idx is None:
         idx = torch.empty(mass.shape, dtype=torch.int32, device=mass.device)
     if count is None:
@@ -167,13 +191,15 @@ def select_per_row(mass, thresholds, rows_per_threshold: int = 1, idx=None, coun
     rows of ``mass`` (flattened over its leading axes); ``thresholds`` is a
     float64 device tensor of ``ceil(rows / rows_per_threshold)`` values.
     Returns ``(idx, count)`` as :func:`select`."""
-    _check_inputs(mass, thresholds)
+    _check_inputs(mass, thresholds, idx, count)
     if mass.dtype != torch.float32 or thresholds.dtype != torch.float64:
         raise TypeError("mass must be float32 and thresholds float64")
     nkb = mass.shape[-1]
     rows = mass.numel() // nkb if nkb else 0
     if thresholds.numel() < (rows + rows_per_threshold - 1) // max(1, rows_per_threshold):
         raise ValueError("too few thresholds for the rows")
+    _check_out(idx, mass.shape, torch.int32, "idx")
+    _check_out(count, mass.shape[:-1], torch.int32, "count")
     if idx is None:
         idx = torch.empty(mass.shape, dtype=torch.int32, device=mass.device)
     if count is None:
@@ -187,13 +213,14 @@ def select_per_row(mass, thresholds, rows_per_threshold: int = 1, idx=None, coun
 
 def block_mask(idx, count, mask=None):
     """The lists as a uint8 mask shaped like ``idx`` (1 = key block kept)."""
-    _check_inputs(idx, count)
+    _check_inputs(idx, count, mask)
     if idx.dtype != torch.int32 or count.dtype != torch.int32:
         raise TypeError("idx and count must be int32")
     nkb = idx.shape[-1]
     rows = idx.numel() // nkb if nkb else 0
     if count.numel() != rows:
         raise ValueError("count must have one entry per row of idx")
+    _check_out(mask, idx.shape, torch.uint8, "mask")
     if mask is None:
         mask = torch.empty(idx.shape, dtype=torch.uint8, device=idx.device)
     lib = _lib.load()
@@ -207,7 +234,7 @@ def retained_mass(lse_kept, lse_dense, block: int = 64, head_dim: int = 128, ret
     mass that the frozen lists cover, from the lse of a sparse pass and of a
     dense pass on the same inputs (both ``[B, H, N]`` float32).  Returns
     ``[B, H, nb]`` float32."""
-    _check_inputs(lse_kept, lse_dense)
+    _check_inputs(lse_kept, lse_dense, retained)
     if lse_kept.shape != lse_dense.shape or lse_kept.dim() != 3:
         raise ValueError("expected two [B, H, N] lse tensors")
     if lse_kept.dtype != torch.float32 or lse_dense.dtype != torch.float32:
@@ -215,6 +242,7 @@ def retained_mass(lse_kept, lse_dense, block: int = 64, head_dim: int = 128, ret
     b, h, n = lse_kept.shape
     nb = num_blocks(n, block)
     desc = _lib.AttnDesc(b, h, n, int(head_dim), int(block), _lib.LOSA_BF16, 0.0)
+    _check_out(retained, (b, h, nb), torch.float32, "retained")
     if retained is None:
         retained = torch.empty((b, h, nb), dtype=torch.float32, device=lse_kept.device)
     lib = _lib.load()
@@ -238,6 +266,8 @@ def sparse_plan(count, block: int = 64, head_dim: int = 128, plan=None):
         raise ValueError("unsupported shape for sparse_plan")
     if plan is None:
         plan = torch.empty(size // 4, dtype=torch.int32, device=count.device)
+    elif plan.dtype != torch.int32 or not plan.is_contiguous():
+        raise TypeError("plan must be a contiguous int32 tensor")
     _lib.check("losa_sparse_plan", lib.losa_sparse_plan(
         desc, _ptr(count), _ptr(plan), plan.numel() * 4, _stream(count)))
     return plan
@@ -257,6 +287,8 @@ def sparse_attn(q, k, v, idx, count, block: int = 64, scale=None, o=None, lse=No
         raise ValueError("idx must be [B,H,nb,nb] and count [B,H,nb]")
     if idx.dtype != torch.int32 or count.dtype != torch.int32:
         raise TypeError("idx and count must be int32")
+    _check_out(o, q.shape, q.dtype, "o")
+    _check_out(lse, (b, h, n), torch.float32, "lse")
     if o is None:
         o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     desc = make_desc(q, block, scale, k, v, o)
@@ -266,6 +298,9 @@ def sparse_attn(q, k, v, idx, count, block: int = 64, scale=None, o=None, lse=No
     if plan is not None:
         if plan.dtype != torch.int32:
             raise TypeError("plan must be int32")
+        # the kernel reads one plan entry per launched workgroup
+        if plan.numel() * 4 < lib.losa_sparse_plan_size(desc):
+            raise ValueError("plan is smaller than sparse_plan makes for these shapes")
         _lib.check("losa_sparse_attn_planned", lib.losa_sparse_attn_planned(
             desc, _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(count), _ptr(plan), _ptr(o),
             _ptr(lse), _stream(q)))

@@ -454,9 +454,8 @@ template <int D, int BLK, int MODE, int ROWS = 128>
 hipError_t launch_b(const AttnParams& p, hipStream_t stream) {
   using G = GeoB<D, BLK, MODE, ROWS>;
   auto kern = attn_bf16_kernel<D, BLK, MODE, ROWS>;
-  static hipError_t attr = hipFuncSetAttribute((const void*)kern,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               G::kLdsBytes);
+  static std::atomic<bool> lds_set[kMaxDevices];
+  const hipError_t attr = set_lds_limit(kern, G::kLdsBytes, lds_set);
   if (attr != hipSuccess) return attr;
   const int wph = (p.nb + G::kQPW - 1) / G::kQPW;
   const int grid = p.order != nullptr ? (int)sparse_plan_slots((long long)wph * (p.items / p.nb))

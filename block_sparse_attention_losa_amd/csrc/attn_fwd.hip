@@ -510,9 +510,8 @@ template <typename T, int D, int BQ, int MODE>
 static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   using G = Geo<T, D, BQ, MODE>;
   auto kern = attn_kernel<T, D, BQ, MODE>;
-  static hipError_t attr = hipFuncSetAttribute((const void*)kern,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               G::kLdsBytes);
+  static std::atomic<bool> lds_set[kMaxDevices];
+  const hipError_t attr = set_lds_limit(kern, G::kLdsBytes, lds_set);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(xcd_grid(p.nb, p.items / p.nb)), dim3(256), G::kLdsBytes, stream, p);
   return hipGetLastError();

@@ -12,6 +12,31 @@ namespace {
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
+// True when no two elements of a [B, H, N, D] view with these element
+// strides (D contiguous) share an address: taken innermost first by stride,
+// every dimension of size > 1 must step past the whole extent of the
+// dimensions inside it.  (Sufficient, and exact for the permuted and sliced
+// layouts a caller hands in.)
+bool disjoint(const losa_attn_desc* d, int64_t sb, int64_t sh, int64_t sn) {
+  int64_t size[3] = {d->batch, d->heads, d->seq_len}, stride[3] = {sb, sh, sn};
+  for (int i = 0; i < 3; ++i)  // order by stride, ascending
+    for (int j = i + 1; j < 3; ++j)
+      if (stride[j] < stride[i]) {
+        const int64_t ts = stride[i], tz = size[i];
+        stride[i] = stride[j];
+        size[i] = size[j];
+        stride[j] = ts;
+        size[j] = tz;
+      }
+  int64_t extent = d->head_dim;
+  for (int i = 0; i < 3; ++i) {
+    if (size[i] == 1) continue;
+    if (stride[i] < extent) return false;
+    extent += stride[i] * (size[i] - 1);
+  }
+  return true;
+}
+
 losa_status check_desc(const losa_attn_desc* d, int32_t* nb_out) {
   if (d == nullptr) return LOSA_ERR_NULL_POINTER;
   if (d->dtype != LOSA_BF16 && d->dtype != LOSA_FP32) return LOSA_ERR_BAD_DTYPE;
@@ -26,15 +51,20 @@ losa_status check_desc(const losa_attn_desc* d, int32_t* nb_out) {
   if (static_cast<int64_t>(d->seq_len) * d->head_dim * 2 >= (int64_t{1} << 31))
     return LOSA_ERR_BAD_SHAPE;
   for (int t = 0; t < 2; ++t) {
-    const int64_t sb = t ? d->o_stride_batch : d->stride_batch;
-    const int64_t sh = t ? d->o_stride_head : d->stride_head;
+    // the stride of a dimension of size 1 never enters an address
+    const int64_t sb = d->batch == 1 ? 0 : (t ? d->o_stride_batch : d->stride_batch);
+    const int64_t sh = d->heads == 1 ? 0 : (t ? d->o_stride_head : d->stride_head);
     const int64_t sn = t ? d->o_stride_token : d->stride_token;
-    if (sb == 0 && sh == 0 && sn == 0) continue;  // contiguous
+    if ((t ? d->o_stride_batch : d->stride_batch) == 0 && (t ? d->o_stride_head : d->stride_head) == 0 &&
+        sn == 0)
+      continue;  // contiguous
     if (d->dtype != LOSA_BF16) return LOSA_ERR_BAD_ARGUMENT;
     if (sn < d->head_dim || sh < 0 || sb < 0) return LOSA_ERR_BAD_ARGUMENT;
     if (sn % 8 || sh % 8 || sb % 8) return LOSA_ERR_MISALIGNED;
     if ((static_cast<int64_t>(d->seq_len) - 1) * sn * 2 + 2 * d->head_dim >= (int64_t{1} << 31))
       return LOSA_ERR_BAD_SHAPE;
+    // outputs must not alias one another (inputs are only read)
+    if (t == 1 && !disjoint(d, sb, sh, sn)) return LOSA_ERR_BAD_ARGUMENT;
   }
   *nb_out = static_cast<int32_t>(nb);
   return LOSA_OK;
@@ -55,11 +85,12 @@ losa::AttnParams base_params(const losa_attn_desc* d, int32_t nb) {
                   cb = ch * d->heads;  // contiguous [B, H, N, D]
   const bool in_c = d->stride_batch == 0 && d->stride_head == 0 && d->stride_token == 0;
   const bool out_c = d->o_stride_batch == 0 && d->o_stride_head == 0 && d->o_stride_token == 0;
-  p.stride_b = in_c ? cb : d->stride_batch;
-  p.stride_h = in_c ? ch : d->stride_head;
+  // strides of size-1 dimensions are never multiplied by a nonzero index
+  p.stride_b = in_c ? cb : (d->batch == 1 ? 0 : d->stride_batch);
+  p.stride_h = in_c ? ch : (d->heads == 1 ? 0 : d->stride_head);
   p.stride_n = in_c ? cn : d->stride_token;
-  p.o_stride_b = out_c ? cb : d->o_stride_batch;
-  p.o_stride_h = out_c ? ch : d->o_stride_head;
+  p.o_stride_b = out_c ? cb : (d->batch == 1 ? 0 : d->o_stride_batch);
+  p.o_stride_h = out_c ? ch : (d->heads == 1 ? 0 : d->o_stride_head);
   p.o_stride_n = out_c ? cn : d->o_stride_token;
   return p;
 }
@@ -316,7 +347,9 @@ const char* losa_status_string(losa_status status) {
     case LOSA_ERR_BAD_THRESHOLD: return "threshold must be > 0 and not NaN";
     case LOSA_ERR_MISALIGNED: return "pointer alignment below the requirement";
     case LOSA_ERR_DEVICE: return "the HIP runtime rejected a launch";
-    case LOSA_ERR_BAD_ARGUMENT: return "invalid argument (scale must be finite and >= 0)";
+    case LOSA_ERR_BAD_ARGUMENT:
+      return "invalid argument (scale not finite or negative, bad strides or aliasing output "
+             "layout, or rows per threshold < 1)";
     case LOSA_ERR_WORKSPACE: return "workspace smaller than the size the library asks for";
   }
   return "unknown status";

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace losa {
 
 // kDenseMass: the dense pass that also writes, per row and key block, the
@@ -33,6 +35,24 @@ struct AttnParams {
   int32_t items;         // B*H*nb work items (one per query block)
   float scale;           // softmax scale c
 };
+
+// Raises kern's dynamic-LDS limit to `bytes` on the current device, once
+// per device: the limit is a per-device attribute of the kernel, so a
+// process that launches on several GPUs sets it on each.  `done` is the
+// calling kernel's own flag array (one flag per device id).
+constexpr int kMaxDevices = 64;
+template <typename Kernel>
+hipError_t set_lds_limit(Kernel kern, int bytes, std::atomic<bool> (&done)[kMaxDevices]) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && dev >= 0 && dev < kMaxDevices)
+    done[dev].store(true, std::memory_order_release);
+  return e;
+}
 
 // Launches one pass over every (batch, head, query block).  dtype: 0 bf16,
 // 1 fp32.  Returns the HIP status of the launch.

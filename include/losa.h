@@ -71,10 +71,13 @@ typedef struct {
    * a token are contiguous) of Q, K and V (shared) and of O.  A triple of 0s
    * means contiguous [B, H, N, D].  Otherwise (bf16 only): token stride >= D,
    * every stride a multiple of 8 elements (16 bytes) and >= 0, and
-   * (N-1)*token_stride*2 + 2*D < 2^31.  Examples: [B, N, H, D] is
-   * (N*H*D, D, H*D); Q of a packed [B, N, 3, H, D] projection is
-   * (3*N*H*D, D, 3*H*D).  lse, mass, idx and count stay contiguous.  The O
-   * layout must not make two output elements alias. */
+   * (N-1)*token_stride*2 + 2*D < 2^31; the stride of a dimension of size 1
+   * is ignored.  Examples: [B, N, H, D] is (N*H*D, D, H*D); Q of a packed
+   * [B, N, 3, H, D] projection is (3*N*H*D, D, 3*H*D).  lse, mass, idx and
+   * count stay contiguous.  An O layout in which two output elements could
+   * share an address (ordered by stride, each dimension of size > 1 must step
+   * past the extent of those inside it) is rejected with
+   * LOSA_ERR_BAD_ARGUMENT. */
   int64_t stride_batch;
   int64_t stride_head;
   int64_t stride_token;
@@ -206,9 +209,11 @@ losa_status losa_retained_mass(const losa_attn_desc* desc, const float* lse_kept
  * idx[b,h,I,0:count[b,h,I]]; the softmax is renormalised over them:
  *   lse'_i = log sum_{j kept} exp(s_ij),  o_i = sum_{j kept} exp(s_ij - lse'_i) v_j.
  * idx/count as produced by losa_select; the lists may be in any order.
- * Entries are trusted: each idx in [0, nb) (others are ignored), no
- * duplicates needed, 1 <= count <= nb.  A query block whose list is empty
- * gets o = 0 and lse' = -inf.
+ * Lists that did not come from losa_select (a file, another tool) are safe
+ * to pass: count is clamped to [0, nb], entries outside [0, nb) are
+ * ignored and a repeated entry counts once, so no list makes the kernel
+ * read outside Q, K, V or the list row.  A query block whose list ends up
+ * empty gets o = 0 and lse' = -inf.
  * o: output [B,H,N,D]; lse: output [B,H,N] fp32 or NULL.
  */
 losa_status losa_sparse_attn(const losa_attn_desc* desc, const void* q, const void* k,
@@ -229,10 +234,13 @@ losa_status losa_sparse_attn(const losa_attn_desc* desc, const void* q, const vo
  * when plan_bytes is below the size.  Items of equal cost may be ordered
  * differently from call to call; results do not depend on the order.
  * losa_sparse_attn_planned computes exactly what losa_sparse_attn computes
- * (bit-identical outputs) in the plan's order.  The plan is trusted like
- * idx/count: it must come from losa_sparse_plan for the same desc and count
- * (entries outside the valid range are skipped, leaving those rows
- * unwritten).  For LOSA_FP32 the plan is ignored.
+ * (bit-identical outputs) in the plan's order.  The plan must hold at
+ * least losa_sparse_plan_size(desc) bytes (the kernel reads one entry per
+ * workgroup it launches; its size is not passed, so this is the caller's
+ * guarantee) and should come from losa_sparse_plan for the same desc: a
+ * plan made from other counts of the same shape is still a complete order,
+ * only a slower one; entries outside the valid range are skipped, leaving
+ * those rows unwritten.  For LOSA_FP32 the plan is ignored.
  */
 int64_t losa_sparse_plan_size(const losa_attn_desc* desc);
 losa_status losa_sparse_plan(const losa_attn_desc* desc, const int32_t* count, int32_t* plan,

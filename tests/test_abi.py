@@ -81,13 +81,36 @@ def test_descriptor_validation(lib, kw, code):
     (dict(stride_batch=16 * 128 * 1000, stride_head=132, stride_token=2 * 128), 5),
     (dict(dtype=1, stride_batch=2 * 128 * 1000, stride_head=128, stride_token=2 * 128), 7),
     (dict(o_stride_token=100), 7),
-    (dict(o_stride_batch=-8, o_stride_head=128, o_stride_token=256), 7),
+    (dict(batch=2, o_stride_batch=-8, o_stride_head=128, o_stride_token=256), 7),
     (dict(seq_len=60000, stride_batch=8, stride_head=8, stride_token=8 * 4096), 2),
+    # output layouts in which two elements would share an address
+    (dict(o_stride_token=128), 7),                               # heads on top of each other
+    (dict(o_stride_head=128, o_stride_token=128), 7),            # head h+1 = token n+1
+    (dict(batch=2, o_stride_batch=256, o_stride_head=128, o_stride_token=256), 7),
 ])
 def test_layout_validation(lib, kw, code):
     d = desc(**kw)
     assert lib.losa_dense_attn(d, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == code
     assert lib.losa_sparse_attn(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == code
+    assert lib.losa_dense_attn_mass_workspace(d) == -1
+
+
+@pytest.mark.parametrize("kw", [
+    # [B, N, H, D] read and written in place
+    dict(batch=2, stride_batch=1000 * 2 * 128, stride_head=128, stride_token=2 * 128,
+         o_stride_batch=1000 * 2 * 128, o_stride_head=128, o_stride_token=2 * 128),
+    # q/k/v of a packed [B, N, 3, H, D] projection, O a [B, N, H, D] tensor
+    dict(batch=2, stride_batch=3 * 1000 * 2 * 128, stride_head=128, stride_token=3 * 2 * 128,
+         o_stride_batch=1000 * 2 * 128, o_stride_head=128, o_stride_token=2 * 128),
+    # O a slice of a wider buffer (token stride above the packed row)
+    dict(o_stride_batch=0, o_stride_head=128, o_stride_token=4 * 128),
+    # a size-1 batch: its stride is never used, whatever its value
+    dict(stride_batch=12, stride_head=128, stride_token=2 * 128,
+         o_stride_batch=-3, o_stride_head=128, o_stride_token=2 * 128),
+])
+def test_layouts_accepted(lib, kw):
+    # the workspace query validates the descriptor and launches nothing
+    assert lib.losa_dense_attn_mass_workspace(desc(**kw)) > 0
 
 
 def test_null_and_alignment(lib):
