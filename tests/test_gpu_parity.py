@@ -190,6 +190,47 @@ def test_repeat_runs_are_bitwise_identical(losa):
         assert np.array_equal(a, b)
 
 
+TAIL_CASES = [(d, blk, t) for d in (64, 128)
+              for blk, tails in ((64, (1, 2, 17, 31, 32, 33, 63)), (128, (1, 63, 64, 65, 127)))
+              for t in tails]
+
+
+@pytest.mark.parametrize("d,blk,tail", TAIL_CASES)
+def test_ragged_tail_sweep(losa, d, blk, tail):
+    """Every path at N = 2 blocks + a tail of 1..block-1 keys (bf16): dense
+    and one-sweep mass against the oracle, the selection on the GPU's masses
+    bit-identical, planned sparse attention against the oracle over the
+    selected lists.  N < 384, so the 256-row dense workgroups run with most
+    of their rows past N."""
+    n = 2 * blk + tail
+    cfg = synth.small_config(n_grid=(1, 1, n), head_dim=d, block=blk, heads=2,
+                             alpha=(3.0, 0.5), seed=100 + tail)
+    _say(f"[parity] tail sweep N={n} D={d} block={blk}")
+    q, k, v = synth.make_inputs(cfg)
+    tq, tk, tv = (_dev(x, "bf16") for x in (q, k, v))
+    nb = cfg.num_blocks
+    o, lse, mass = losa.dense_attn_mass(tq, tk, tv, block=blk)
+    idx, cnt = losa.select(mass, 0.9)
+    plan = losa.sparse_plan(cnt, block=blk, head_dim=d)
+    so, slse = losa.sparse_attn(tq, tk, tv, idx, cnt, block=blk, want_lse=True, plan=plan)
+    torch.cuda.synchronize()
+    o_g, lse_g, mass_g = _np(o), _np(lse), _np(mass)
+    idx_g, cnt_g, so_g, slse_g = _np(idx), _np(cnt), _np(so), _np(slse)
+    for h in range(cfg.heads):
+        od, lsed = oracle.dense_attention(q[0, h], k[0, h], v[0, h])
+        _compare_attention(o_g[0, h], lse_g[0, h], od, lsed, f"tail N={n} dense h{h}")
+        md = oracle.block_mass(q[0, h], k[0, h], blk, lse=lsed)
+        merr = np.abs(mass_g[0, h].astype(np.float64) - md).max()
+        assert merr <= MASS_ATOL, f"tail N={n} mass h{h} err {merr:.3e}"
+        ridx, rcnt = oracle.select(mass_g[0, h], 0.9)
+        assert np.array_equal(cnt_g[0, h], rcnt), f"tail N={n} counts h{h}"
+        for i in range(nb):
+            assert np.array_equal(idx_g[0, h, i, :rcnt[i]], ridx[i, :rcnt[i]])
+        ref_o, ref_lse = oracle.sparse_attention(q[0, h], k[0, h], v[0, h], idx_g[0, h],
+                                                 cnt_g[0, h], blk)
+        _compare_attention(so_g[0, h], slse_g[0, h], ref_o, ref_lse, f"tail N={n} sparse h{h}")
+
+
 @pytest.mark.parametrize("d,blk,dtype", [(128, 64, "bf16"), (64, 128, "bf16"),
                                          (64, 64, "fp32")])
 def test_sparse_arbitrary_lists(losa, d, blk, dtype):
