@@ -183,6 +183,8 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[mt][i] = 0.f;
   float m_run = -INFINITY;  // reference max (log2 domain) of the exp2 arguments
+  float m_thr = -INFINITY;  // m_run + kRaise: a tile whose scaled max passes it raises m_run
+  float m_use = 0.f;        // m_run, or 0 while it is -inf (no finite score yet)
   float l_run = 0.f;        // this lane's partial row sum
   const float c2 = p.scale * kLog2e;
   float lse_row = 0.f;      // kMass: the row's lse (natural), +inf on padding rows
@@ -255,7 +257,10 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
       if (lane == 0) part[wave * G::kMaxBlocks + (key0 / BLK)] += acc;
     } else {
       // online softmax; the reference max is raised only when a probability
-      // could exceed 2^kRaise, so O is rarely rescaled
+      // could exceed 2^kRaise, so O is rarely rescaled.  Everything that
+      // depends on a raise (the new reference, the rescale factor alpha)
+      // lives in a wave-uniform branch taken on those rare tiles; elsewhere
+      // alpha is 1, and l + lsum is what fma(l, 1, lsum) rounds to.
       float mx = -INFINITY;
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
@@ -263,10 +268,26 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[cc][i]);
       mx = pair_max(mx);
       const float m_cand = mx * c2;
-      const bool raise = m_cand > m_run + kRaise;
-      const float m_new = raise ? m_cand : m_run;
-      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const bool raise = m_cand > m_thr;
+      const bool any_raise = __ballot(raise) != 0;
+      float alpha = 1.0f;
+      if (any_raise) {
+        if (raise) {
+          alpha = __builtin_amdgcn_exp2f(m_run - m_cand);
+          m_run = m_cand;
+          m_thr = m_run + kRaise;
+          m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        }
+        // O is not touched by the exponentials below, so rescaling it here
+        // (rather than just before the P V products) gives the same bits,
+        // and keeps the whole raise path in one branch
+        if constexpr (G::kWithV) {
+#pragma unroll
+          for (int mt = 0; mt < kORegs; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[mt][i] *= alpha;
+        }
+      }
       float pr[2][16];
       float lsum = 0.f;
 #pragma unroll
@@ -276,8 +297,7 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
           pr[cc][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][i], c2, -m_use));
           lsum += pr[cc][i];
         }
-      l_run = __builtin_fmaf(l_run, alpha, lsum);
-      m_run = m_new;
+      l_run = any_raise ? __builtin_fmaf(l_run, alpha, lsum) : l_run + lsum;
       if constexpr (MODE == kDenseMass) {
         // the tile's part of the row sum (both lanes of the row), against
         // the current reference and accumulated over the key block's tiles;
@@ -285,7 +305,8 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
         // -- at the start of the next step, ahead of that step's tile loads:
         // stores count in vmcnt, and a store issued here would make the
         // end-of-step wait for the loads also wait for its write-back
-        tacc = __builtin_fmaf(tacc, alpha, pair_sum(lsum));
+        const float tsum = pair_sum(lsum);
+        tacc = any_raise ? __builtin_fmaf(tacc, alpha, tsum) : tacc + tsum;
         if (G::kSubs == 1 || (key0 % BLK) == BLK - 64 || key0 + 64 >= N) {
           const int kb = key0 / BLK;
           if (kb == 0) m0 = m_run;
@@ -295,12 +316,6 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
         }
       }
       if constexpr (G::kWithV) {
-        if (__ballot(raise)) {
-#pragma unroll
-          for (int mt = 0; mt < kORegs; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[mt][i] *= alpha;
-        }
         const unsigned char* vs = vslot[t & 1];
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {

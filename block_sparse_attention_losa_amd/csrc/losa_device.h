@@ -54,10 +54,13 @@ __device__ __forceinline__ float pair_sum(float x) {
   lane_halves(x, lo, hi);
   return lo + hi;
 }
+// The max is taken inside the same asm block: fmaxf on the asm outputs
+// would first canonicalize both (two more VALU ops on the softmax's path).
 __device__ __forceinline__ float pair_max(float x) {
-  float lo, hi;
-  lane_halves(x, lo, hi);
-  return fmaxf(lo, hi);
+  float a = x, b = x;
+  asm("s_nop 1\n\tv_permlane32_swap_b32_e64 %0, %1 fi:1\n\ts_nop 0\n\tv_max_f32 %0, %0, %1"
+      : "+v"(a), "+v"(b));
+  return a;
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
