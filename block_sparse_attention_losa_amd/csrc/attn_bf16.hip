@@ -338,16 +338,48 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
     }
   };
 
+  // Sparse at D = 128: the list entries of tiles t, t+1 and t+2 as read
+  // from LDS (the same value in every lane), carried from step to step.
+  // Each step reads the entry of tile t+3, a step before its first use, so
+  // the loop never waits on an LDS read of the list (reading entries t, t+1,
+  // t+2 where they are used costs one LDS round trip each, per step):
+  // measured 1.2 % faster.  At D = 64 the three registers add spills in the
+  // three-waves-per-SIMD budget and it is 2 % slower, so that kernel reads
+  // the entries where they are used.
+  constexpr bool kWindow = MODE == kSparse && D == 128;
+  int win0 = 0, win1 = 0, win2 = 0;
+  auto raw_entry = [&](int t) -> int {
+    if constexpr (MODE == kSparse)
+      return list[G::kSubs == 1 ? t : (t >> 1)];
+    else
+      return 0;
+  };
+  auto key0_from = [&](int e, int t) -> int {
+    return (e & 0xFFFF) * BLK + (G::kSubs == 1 ? 0 : (t & 1) * 64);
+  };
+
   // One pipelined step.  `masked` is true only for a final tile that runs
   // past the sequence end (ascending lists put the short last block last).
   auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2], auto masked) {
-    const int key0 = key0_of(t);
+    int e0 = 0, e1 = 0, e2 = 0;
+    if constexpr (kWindow) {
+      e0 = __builtin_amdgcn_readfirstlane(win0);
+      e1 = __builtin_amdgcn_readfirstlane(win1);
+      e2 = __builtin_amdgcn_readfirstlane(win2);
+      win0 = win1;
+      win1 = win2;
+      win2 = t + 3 < ntile ? raw_entry(t + 3) : 0;
+    }
+    const int key0 = kWindow ? key0_from(e0, t) : key0_of(t);
     flush_rowsum();
     // loads for later tiles: K(t+2) into the K slot freed by tile t, V(t+1)
     // into the V slot freed by tile t-1
-    if (t + 2 < ntile) dma_tile(kh, key0_of(t + 2), kslot[t & 1], koff);
+    if (t + 2 < ntile)
+      dma_tile(kh, kWindow ? key0_from(e2, t + 2) : key0_of(t + 2), kslot[t & 1], koff);
     if constexpr (G::kWithV)
-      if (t + 1 < ntile) dma_tile(vh, key0_of(t + 1), vslot[(t + 1) & 1], voff);
+      if (t + 1 < ntile)
+        dma_tile(vh, kWindow ? key0_from(e1, t + 1) : key0_of(t + 1),
+                 vslot[(t + 1) & 1], voff);
     // Wave priority: the next tile's score MFMAs issue at the lowest level,
     // everything else (softmax, P V, loads, the barrier) one above.  The two
     // waves sharing a SIMD come from different workgroups; when one is in its
@@ -361,7 +393,7 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
       __builtin_amdgcn_s_setprio(0);
       compute_s(kslot[(t + 1) & 1], sn);
       __builtin_amdgcn_s_setprio(1);
-      if (member(t)) consume(t, key0, sc, masked);
+      if (kWindow ? ((e0 >> (16 + qi)) & 1) != 0 : member(t)) consume(t, key0, sc, masked);
     } else {
       // scores of the next tile; after the last tile this reads a stale
       // slot and the result is dropped, which keeps the block branch-free
@@ -395,6 +427,11 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
     __syncthreads();  // K slot 0 may be refilled from here on
   }
   const bool last_short = ntile > 0 && key0_of(ntile - 1) + 64 > N;
+  if constexpr (kWindow) {
+    win0 = ntile > 0 ? raw_entry(0) : 0;
+    win1 = ntile > 1 ? raw_entry(1) : 0;
+    win2 = ntile > 2 ? raw_entry(2) : 0;
+  }
   const int nplain = ntile - (last_short ? 1 : 0);
   int t = 0;
   for (; t + 1 < nplain; t += 2) {
