@@ -107,6 +107,17 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   const int row = w * G::kRows + wave * 32 + l32;
   const bool row_ok = row < N;
 
+  // ---- Q^T as the B operand, in registers (loaded first: the loads overlap
+  // the list build below)
+  bf16x8 qreg[D / 16];
+  {
+    // rows past N lie beyond the range and read as zero
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qh, (N - 1) * row_stride + G::kRowBytes);
+#pragma unroll
+    for (int dk = 0; dk < D / 16; ++dk)
+      qreg[dk] = __builtin_bit_cast(bf16x8, buf_load16(qr, row * row_stride + dk * 32 + g * 16));
+  }
+
   // ---- key blocks visited, in ascending order, with member bits
   int nblk = nb;
   const int* list = nullptr;
@@ -115,8 +126,8 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
     int* lst = flag + G::kMaxBlocks;
     int* ccount = lst + G::kMaxBlocks;
     const int qb0 = w * G::kQPW;
-    nblk = build_union_list<G::kQPW, G::kThreads>(p.idx, p.cnt, (size_t)bh * nb + qb0,
-                                                  min(G::kQPW, nb - qb0), nb, flag, lst, ccount);
+    nblk = build_union_list<G::kQPW, G::kThreads, G::kMaxBlocks>(
+        p.idx, p.cnt, (size_t)bh * nb + qb0, min(G::kQPW, nb - qb0), nb, flag, lst, ccount);
     list = lst;
   }
   float* part = nullptr;  // kMass: per-wave partial tile sums [4][nb]
@@ -139,16 +150,6 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
     return (entry_at(t) & 0xFFFF) * BLK + (G::kSubs == 1 ? 0 : (t & 1) * 64);
   };
   auto member = [&](int t) -> bool { return ((entry_at(t) >> (16 + qi)) & 1) != 0; };
-
-  // ---- Q^T as the B operand, in registers
-  bf16x8 qreg[D / 16];
-  {
-    // rows past N lie beyond the range and read as zero
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qh, (N - 1) * row_stride + G::kRowBytes);
-#pragma unroll
-    for (int dk = 0; dk < D / 16; ++dk)
-      qreg[dk] = __builtin_bit_cast(bf16x8, buf_load16(qr, row * row_stride + dk * 32 + g * 16));
-  }
 
   // ---- LDS ring: K tiles at slots 0/1, V tiles at slots 2/3
   unsigned char* kslot[2] = {smem, smem + G::kTileBytes};

@@ -56,28 +56,38 @@ __device__ __forceinline__ v4i16 ds_read_tr16(const unsigned char* p) {
 
 // Union of the frozen lists of up to kQPW query blocks, ascending, written
 // to list[] as (block | member_bits << 16); returns its length.  Called by
-// all kThreads threads of the workgroup.
-template <int kQPW, int kThreads = 256>
+// all kThreads threads of the workgroup; nb <= kMaxLen.
+template <int kQPW, int kThreads = 256, int kMaxLen = 1024>
 __device__ int build_union_list(const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
                                 size_t row0, int nrows, int nb, int* flag, int* list,
                                 int* ccount) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nchunks = (nb + 63) >> 6;
   constexpr int kWaves = kThreads / 64;
+  constexpr int kPer = (kMaxLen + kThreads - 1) / kThreads;  // entries per thread and row
   for (int j = tid; j < nchunks * 64; j += kThreads) flag[j] = 0;
-  __syncthreads();
+  // every entry this thread handles is loaded before any is used, so the
+  // loads overlap instead of each waiting on the one before it
+  int ent[kQPW][kPer];
 #pragma unroll
   for (int q = 0; q < kQPW; ++q) {
-    if (q < nrows) {
-      const int c = min(max(cnt[row0 + q], 0), nb);  // never read past the row
-      const int32_t* row = idx + (row0 + q) * nb;
-      for (int t = tid; t < c; t += kThreads) {
-        const int j = row[t];
-        if ((unsigned)j < (unsigned)nb) flag[j] |= 1 << q;
-      }
+    const int c = q < nrows ? min(max(cnt[row0 + q], 0), nb) : 0;  // never read past the row
+    const int32_t* row = idx + (row0 + q) * nb;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int t = tid + r * kThreads;
+      ent[q][r] = t < c ? row[t] : -1;
     }
-    __syncthreads();
   }
+  __syncthreads();  // flags zeroed
+#pragma unroll
+  for (int q = 0; q < kQPW; ++q)
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int j = ent[q][r];
+      if ((unsigned)j < (unsigned)nb) atomicOr(&flag[j], 1 << q);
+    }
+  __syncthreads();
   for (int c = wave; c < nchunks; c += kWaves) {
     const unsigned long long m = __ballot(flag[c * 64 + lane] != 0);
     if (lane == 0) ccount[c] = __popcll(m);
