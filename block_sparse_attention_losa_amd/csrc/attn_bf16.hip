@@ -205,17 +205,40 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
 
   // S^T of this wave's 32 rows against both 32-key chunks of the K tile
   const int prow = perm_row(l32);
+  // At D = 128 the two 32-key chunks' MFMA chains are interleaved, one step
+  // of each per head-dim slice, with both chunks' K fragments of a slice read
+  // together (measured ~1 % faster there; at D = 64 the chunk-by-chunk order
+  // is as fast or faster).  Either way each chunk accumulates its slices in
+  // the same order, so the scores are the same bits.
   auto compute_s = [&](const unsigned char* slot, f32x16 (&sc)[2]) {
+    if constexpr (D == 128) {
+      const int r0 = prow, r1 = 32 + prow;
+      const unsigned char* krow0 = slot + r0 * G::kRowBytes;
+      const unsigned char* krow1 = slot + r1 * G::kRowBytes;
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const int r = cc * 32 + prow;
-      const unsigned char* krow = slot + r * G::kRowBytes;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sc[cc][i] = 0.f;
+      for (int i = 0; i < 16; ++i) {
+        sc[0][i] = 0.f;
+        sc[1][i] = 0.f;
+      }
 #pragma unroll
       for (int dk = 0; dk < D / 16; ++dk) {
-        const bf16x8 a = *(const bf16x8*)(krow + swz_k<D>(r, 2 * dk + g) * 16);
-        sc[cc] = mfma_bf16(a, qreg[dk], sc[cc]);
+        const bf16x8 a0 = *(const bf16x8*)(krow0 + swz_k<D>(r0, 2 * dk + g) * 16);
+        const bf16x8 a1 = *(const bf16x8*)(krow1 + swz_k<D>(r1, 2 * dk + g) * 16);
+        sc[0] = mfma_bf16(a0, qreg[dk], sc[0]);
+        sc[1] = mfma_bf16(a1, qreg[dk], sc[1]);
+      }
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int r = cc * 32 + prow;
+        const unsigned char* krow = slot + r * G::kRowBytes;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[cc][i] = 0.f;
+#pragma unroll
+        for (int dk = 0; dk < D / 16; ++dk) {
+          const bf16x8 a = *(const bf16x8*)(krow + swz_k<D>(r, 2 * dk + g) * 16);
+          sc[cc] = mfma_bf16(a, qreg[dk], sc[cc]);
+        }
       }
     }
   };
