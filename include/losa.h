@@ -21,11 +21,16 @@
  *    N - (nb-1)*block remaining tokens.  fp32/int32 arrays must be 4-byte
  *    aligned.
  *  - Every pointer argument is a device pointer owned by the caller; the
- *    library never allocates, frees or synchronises, keeps no state between
- *    calls and may be called from several host threads at once.  Outputs
- *    must not overlap inputs.
+ *    library never allocates, frees or synchronises and may be called from
+ *    several host threads at once.  Its only state is set once per kernel
+ *    and device on first use: the kernel's dynamic-LDS limit
+ *    (hipFuncSetAttribute).  Outputs must not overlap inputs.
  *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
- *    Work is enqueued asynchronously on it.
+ *    Work is enqueued asynchronously on it, as kernel launches only (no
+ *    memset or copy), so calls on different streams may run concurrently
+ *    and calls can be captured into a HIP graph and replayed; make one call
+ *    of each entry point on the device before capturing, so that the
+ *    first-use attribute is not set inside the capture.
  *  - Arguments are validated on the host before anything is enqueued; a
  *    status other than LOSA_OK means nothing was launched.  A launch the HIP
  *    runtime rejects returns LOSA_ERR_DEVICE.  Faults while the kernels run
