@@ -367,10 +367,11 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   // Each step reads the entry of tile t+3, a step before its first use, so
   // the loop never waits on an LDS read of the list (reading entries t, t+1,
   // t+2 where they are used costs one LDS round trip each, per step):
-  // measured 1.2 % faster.  At D = 64 the three registers add spills in the
-  // three-waves-per-SIMD budget and it is 2 % slower, so that kernel reads
-  // the entries where they are used.
+  // measured 1.2 % faster.  At D = 64 the three carried registers add spills
+  // in the three-waves-per-SIMD budget (2 % slower), so that kernel reads the
+  // step's three entries together at its start instead: one wait per step.
   constexpr bool kWindow = MODE == kSparse && D == 128;
+  constexpr bool kBatch = MODE == kSparse && !kWindow;
   int win0 = 0, win1 = 0, win2 = 0;
   auto raw_entry = [&](int t) -> int {
     if constexpr (MODE == kSparse)
@@ -393,16 +394,24 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
       win0 = win1;
       win1 = win2;
       win2 = t + 3 < ntile ? raw_entry(t + 3) : 0;
+    } else if constexpr (kBatch) {
+      const int r0 = raw_entry(t);
+      const int r1 = t + 1 < ntile ? raw_entry(t + 1) : 0;
+      const int r2 = t + 2 < ntile ? raw_entry(t + 2) : 0;
+      e0 = __builtin_amdgcn_readfirstlane(r0);
+      e1 = __builtin_amdgcn_readfirstlane(r1);
+      e2 = __builtin_amdgcn_readfirstlane(r2);
     }
-    const int key0 = kWindow ? key0_from(e0, t) : key0_of(t);
+    constexpr bool kHave = kWindow || kBatch;
+    const int key0 = kHave ? key0_from(e0, t) : key0_of(t);
     flush_rowsum();
     // loads for later tiles: K(t+2) into the K slot freed by tile t, V(t+1)
     // into the V slot freed by tile t-1
     if (t + 2 < ntile)
-      dma_tile(kh, kWindow ? key0_from(e2, t + 2) : key0_of(t + 2), kslot[t & 1], koff);
+      dma_tile(kh, kHave ? key0_from(e2, t + 2) : key0_of(t + 2), kslot[t & 1], koff);
     if constexpr (G::kWithV)
       if (t + 1 < ntile)
-        dma_tile(vh, kWindow ? key0_from(e1, t + 1) : key0_of(t + 1),
+        dma_tile(vh, kHave ? key0_from(e1, t + 1) : key0_of(t + 1),
                  vslot[(t + 1) & 1], voff);
     // Wave priority: the next tile's score MFMAs issue at the lowest level,
     // everything else (softmax, P V, loads, the barrier) one above.  The two
@@ -417,7 +426,7 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
       __builtin_amdgcn_s_setprio(0);
       compute_s(kslot[(t + 1) & 1], sn);
       __builtin_amdgcn_s_setprio(1);
-      if (kWindow ? ((e0 >> (16 + qi)) & 1) != 0 : member(t)) consume(t, key0, sc, masked);
+      if (((e0 >> (16 + qi)) & 1) != 0) consume(t, key0, sc, masked);
     } else {
       // scores of the next tile; after the last tile this reads a stale
       // slot and the result is dropped, which keeps the block branch-free
