@@ -16,6 +16,34 @@
 
 namespace losa {
 
+// The value of v held by lane l ^ lj.  Distances 1 and 2 are quad
+// permutations, 4 a mirror of each 8-lane half row (lane i reads i ^ 7)
+// followed by a quad reversal (i ^ 3), and 8 a rotation of each 16-lane row
+// by 8 (the same as xor 8 there): DPP moves, ordinary VALU work with no
+// wait.  Distances 16 and 32 cross rows and go through ds_bpermute.
+__device__ __forceinline__ unsigned long long lane_xor64(unsigned long long v, int lj) {
+  const int lo = (int)(unsigned)v, hi = (int)(unsigned)(v >> 32);
+  int rlo, rhi;
+  if (lj == 1) {
+    rlo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+    rhi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, true);
+  } else if (lj == 2) {
+    rlo = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+    rhi = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, true);
+  } else if (lj == 4) {
+    rlo = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(lo, 0x141, 0xF, 0xF, true), 0x1B,
+                                   0xF, 0xF, true);  // row_half_mirror, quad_perm [3,2,1,0]
+    rhi = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(hi, 0x141, 0xF, 0xF, true), 0x1B,
+                                   0xF, 0xF, true);
+  } else if (lj == 8) {
+    rlo = __builtin_amdgcn_mov_dpp(lo, 0x128, 0xF, 0xF, true);  // row_ror:8
+    rhi = __builtin_amdgcn_mov_dpp(hi, 0x128, 0xF, 0xF, true);
+  } else {
+    return __shfl_xor(v, lj, 64);
+  }
+  return ((unsigned long long)(unsigned)rhi << 32) | (unsigned)rlo;
+}
+
 template <int E>
 __global__ void __launch_bounds__(256) select_kernel(const float* __restrict__ mass, int rows,
                                                      int nkb, double tau,
@@ -43,36 +71,35 @@ __global__ void __launch_bounds__(256) select_kernel(const float* __restrict__ m
   }
 
   // bitonic sort, descending: in a k-block whose (e & k) == 0 the lower
-  // position keeps the larger key
+  // position keeps the larger key.  Each compare-exchange is one 64-bit
+  // compare whose outcome is flipped by the block's direction, then one
+  // select per word.  For k < E the direction depends only on r, for
+  // k >= E only on the lane (e = lane * E + r).
 #pragma unroll
   for (int k = 2; k <= 64 * E; k <<= 1) {
+    const bool lane_desc = ((lane * E) & k) == 0;  // the direction when k >= E
 #pragma unroll
     for (int j = k >> 1; j >= 1; j >>= 1) {
       if (j >= E) {
         const int lj = j / E;
         const bool lower = (lane & lj) == 0;
+        const bool take_max = (lower == lane_desc);  // here k > j >= E
 #pragma unroll
         for (int r = 0; r < E; ++r) {
-          const unsigned long long other = __shfl_xor(key[r], lj, 64);
-          const int e = lane * E + r;
-          const bool desc = (e & k) == 0;
-          const bool take_max = (lower == desc);
-          const unsigned long long hi = key[r] > other ? key[r] : other;
-          const unsigned long long lo = key[r] > other ? other : key[r];
-          key[r] = take_max ? hi : lo;
+          const unsigned long long other = lane_xor64(key[r], lj);
+          const bool keep = (key[r] > other) == take_max;
+          key[r] = keep ? key[r] : other;
         }
       } else {
 #pragma unroll
         for (int r = 0; r < E; ++r) {
           if ((r & j) == 0) {
             const int r2 = r | j;
-            const int e = lane * E + r;
-            const bool desc = (e & k) == 0;
+            const bool desc = k < E ? ((r & k) == 0) : lane_desc;
             const unsigned long long a = key[r], b = key[r2];
-            const unsigned long long hi = a > b ? a : b;
-            const unsigned long long lo = a > b ? b : a;
-            key[r] = desc ? hi : lo;
-            key[r2] = desc ? lo : hi;
+            const bool swap = (a < b) == desc;
+            key[r] = swap ? b : a;
+            key[r2] = swap ? a : b;
           }
         }
       }
