@@ -74,8 +74,8 @@ def _check_selection_properties(mass, idx, cnt, tau):
                 assert tot[-2] < tau, r
 
 
-def _run_config(losa, cid, taus, later_step=None, n_heads_checked=3, seed=0):
-    cfg = synth.CONFIGS[cid]
+def _run_config(losa, cid, taus, later_step=None, n_heads_checked=3, seed=0, cfg=None):
+    cfg = synth.CONFIGS[cid] if cfg is None else cfg
     rng = np.random.default_rng(seed)
     _say(f"[fullsize] config {cid}: generating {cfg.name}")
     q, k, v = synth.make_inputs(cfg)
@@ -197,3 +197,17 @@ def test_hunyuan(losa):
 def test_cogvideox_tau_sweep(losa):
     kept = _run_config(losa, 5, (0.95, 0.99, 0.999, 1.0))
     assert kept[0.95] <= kept[0.99] <= kept[0.999] <= kept[1.0] == 1.0
+
+
+@pytest.mark.parametrize("n_grid,d,blk", [((1, 256, 256), 64, 64), ((2, 256, 256), 128, 128)])
+def test_max_blocks(losa, n_grid, d, blk):
+    """nb = 1024 key blocks, the most the library takes: the sparse
+    kernel's union list and flags fill their LDS arrays exactly, and the
+    selection sorts full 1024-key rows."""
+    cfg = synth.small_config(n_grid=n_grid, head_dim=d, block=blk, heads=1, alpha=(2.0,),
+                             seed=77)
+    assert cfg.num_blocks == 1024
+    # tau 1 keeps every block: each workgroup's union list is all 1024
+    kept = _run_config(losa, f"max N={cfg.seq_len}", (0.9, 0.99, 1.0), n_heads_checked=1,
+                       cfg=cfg)
+    assert 0.0 < kept[0.9] <= kept[0.99] < kept[1.0] == 1.0
