@@ -321,7 +321,9 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
           pr[cc][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][i], c2, -m_use));
           lsum += pr[cc][i];
         }
-      l_run = any_raise ? __builtin_fmaf(l_run, alpha, lsum) : l_run + lsum;
+      // alpha is 1 unless the wave raised, and fma(l, 1, x) rounds exactly
+      // like l + x
+      l_run = __builtin_fmaf(l_run, alpha, lsum);
       if constexpr (MODE == kDenseMass) {
         // the tile's part of the row sum (both lanes of the row), against
         // the current reference and accumulated over the key block's tiles;
@@ -330,7 +332,7 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
         // stores count in vmcnt, and a store issued here would make the
         // end-of-step wait for the loads also wait for its write-back
         const float tsum = pair_sum(lsum);
-        tacc = any_raise ? __builtin_fmaf(tacc, alpha, tsum) : tacc + tsum;
+        tacc = __builtin_fmaf(tacc, alpha, tsum);
         if (G::kSubs == 1 || (key0 % BLK) == BLK - 64 || key0 + 64 >= N) {
           const int kb = key0 / BLK;
           if (kb == 0) m0 = m_run;
@@ -393,11 +395,15 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
       e2 = __builtin_amdgcn_readfirstlane(win2);
       win0 = win1;
       win1 = win2;
-      win2 = t + 3 < ntile ? raw_entry(t + 3) : 0;
+      // read without a bounds test: past the list it lands in the counts
+      // that follow it in LDS, and the value is then never used
+      win2 = raw_entry(t + 3);
     } else if constexpr (kBatch) {
+      // entries t+1, t+2 are read even past the list (into the counts that
+      // follow it in LDS); the loads below use them only when in range
       const int r0 = raw_entry(t);
-      const int r1 = t + 1 < ntile ? raw_entry(t + 1) : 0;
-      const int r2 = t + 2 < ntile ? raw_entry(t + 2) : 0;
+      const int r1 = raw_entry(t + 1);
+      const int r2 = raw_entry(t + 2);
       e0 = __builtin_amdgcn_readfirstlane(r0);
       e1 = __builtin_amdgcn_readfirstlane(r1);
       e2 = __builtin_amdgcn_readfirstlane(r2);
