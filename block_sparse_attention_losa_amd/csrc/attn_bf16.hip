@@ -101,7 +101,11 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   const bf16* __restrict__ kh = (const bf16*)p.k + head_off;
   const bf16* __restrict__ vh = (const bf16*)p.v + head_off;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // wave is the same in every lane; saying so once keeps everything derived
+  // from it (LDS slot bases of the tile loads, the wave's rows) in scalar
+  // registers instead of re-deriving it per use
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int qi = wave / G::kWavesPerBlock;  // this wave's query block within the workgroup
   const int row = w * G::kRows + wave * 32 + l32;
