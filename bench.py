@@ -17,7 +17,6 @@ GPU.
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
