@@ -389,6 +389,12 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
     return (e & 0xFFFF) * BLK + (G::kSubs == 1 ? 0 : (t & 1) * 64);
   };
 
+  // Wave priorities (below) pay off when the two waves sharing a SIMD come
+  // from different workgroups, whose steps drift apart; in a 256-row
+  // workgroup (one per CU) both are in the same workgroup, in lockstep, and
+  // equal priorities are 1.3 % faster there.
+  constexpr bool kPrio = ROWS == 128;
+
   // One pipelined step.  `masked` is true only for a final tile that runs
   // past the sequence end (ascending lists put the short last block last).
   auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2], auto masked) {
@@ -423,26 +429,27 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
       if (t + 1 < ntile)
         dma_tile(vh, kHave ? key0_from(e1, t + 1) : key0_of(t + 1),
                  vslot[(t + 1) & 1], voff);
-    // Wave priority: the next tile's score MFMAs issue at the lowest level,
-    // everything else (softmax, P V, loads, the barrier) one above.  The two
-    // waves sharing a SIMD come from different workgroups; when one is in its
-    // softmax (the critical path to its P V MFMAs) and the other in its score
-    // MFMAs, the softmax issues first and the score MFMAs fill its stalls
-    // (measured: 2-3 % faster than equal priorities).
+    // Wave priority (128-row workgroups): the next tile's score MFMAs issue
+    // at the lowest level, everything else (softmax, P V, loads, the
+    // barrier) one above.  The two waves sharing a SIMD come from different
+    // workgroups; when one is in its softmax (the critical path to its P V
+    // MFMAs) and the other in its score MFMAs, the softmax issues first and
+    // the score MFMAs fill its stalls (measured: 1-3 % faster than equal
+    // priorities).
     if constexpr (MODE == kSparse) {
       // waves skip the softmax and P V of tiles their query block did not
       // keep; the next tile's scores are computed regardless (the union
       // exceeds each list by ~3 %), which keeps that work branch-free
-      __builtin_amdgcn_s_setprio(0);
+      if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
       compute_s(kslot[(t + 1) & 1], sn);
-      __builtin_amdgcn_s_setprio(1);
+      if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
       if (((e0 >> (16 + qi)) & 1) != 0) consume(t, key0, sc, masked);
     } else {
       // scores of the next tile; after the last tile this reads a stale
       // slot and the result is dropped, which keeps the block branch-free
-      __builtin_amdgcn_s_setprio(0);
+      if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
       compute_s(kslot[(t + 1) & 1], sn);
-      __builtin_amdgcn_s_setprio(1);
+      if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
       consume(t, key0, sc, masked);
     }
     wait_dma_all();
