@@ -1,168 +1,285 @@
 // Threshold selection of the LoSA construction step on gfx950.
 //
-// One wavefront per query block (row of the mass map).  The row's nkb
-// masses become 64-bit keys (fp32 bit pattern << 32 | ~block index): masses
-// are >= +0, so the bit pattern orders like the value, and the complemented
-// index breaks ties toward the smaller block.  The keys are sorted
-// descending in registers by a bitonic network (E = pow2(nkb)/64 keys per
-// lane; exchanges across lanes via cross-lane shuffles), then a float64
-// prefix sum in sorted order finds the first position where the running mass
-// reaches the threshold.  Float64 sums of float32 masses >= 2^-30 are exact
-// below 1 under any association, so the parallel scan decides exactly like
-// a sequential accumulation.  The threshold is one value for every row, or
-// (per-row variant) taus[row / rows_per_tau] read from device memory.
+// Per row of the mass map: order the key blocks by descending mass (ties
+// toward the smaller block index), accumulate the masses in that order in
+// float64, and keep the shortest prefix whose sum reaches the threshold.
+//
+// A row's nkb masses become 64-bit keys (fp32 bit pattern << 30 | 2^30-1-J):
+// masses are >= +0, so the pattern orders like the value, and the
+// complemented index breaks ties toward the smaller block.  Read as IEEE
+// doubles these keys are finite and non-negative (the top three bits are
+// zero, so the exponent field is at most 0x1FF) and order exactly like the
+// integers; a mass of 0 gives a denormal double, which these kernels keep
+// (float64 denormals are enabled).  A compare-exchange inside a lane is then
+// one v_max_f64 and one v_min_f64 (float64 max and min issue at full rate,
+// float64 compares far slower).  The keys are sorted by a bitonic network
+// over P = pow2(nkb) positions held by L lanes, E = P/L per lane
+// (position = lane * E + register), with E = 16 and L = P/16 for long rows
+// and L = 16 for short ones (measured fastest: enough exchanges stay inside
+// a lane while registers stay below ~100, so several waves share a SIMD).
+// Exchanges at distances below E stay in a lane, lane distances 1-8 are DPP
+// moves inside a 16-lane row and 16, 32 ds_bpermute.  Where the direction of
+// a bitonic block depends on the lane, the lane's keys are negated for that
+// stage (min(a, b) = -max(-a, -b)), so every exchange in the stage keeps the
+// larger value at the lower position.  A float64 prefix sum in sorted order
+// then finds the first position where the running mass reaches the
+// threshold.  Float64 sums of float32 masses >= 2^-30 are exact below 1
+// under any association, so the parallel scan decides exactly like a
+// sequential accumulation.  The threshold is one value for every row, or
+// (per-row variant) taus[row / rows_per_tau].
 #include "losa_device.h"
 #include "losa_launch.h"
 
 namespace losa {
 
-// The value of v held by lane l ^ lj.  Distances 1 and 2 are quad
-// permutations, 4 a mirror of each 8-lane half row (lane i reads i ^ 7)
-// followed by a quad reversal (i ^ 3), and 8 a rotation of each 16-lane row
-// by 8 (the same as xor 8 there): DPP moves, ordinary VALU work with no
-// wait.  Distances 16 and 32 cross rows and go through ds_bpermute.
-__device__ __forceinline__ unsigned long long lane_xor64(unsigned long long v, int lj) {
-  const int lo = (int)(unsigned)v, hi = (int)(unsigned)(v >> 32);
-  int rlo, rhi;
-  if (lj == 1) {
-    rlo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
-    rhi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, true);
-  } else if (lj == 2) {
-    rlo = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
-    rhi = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, true);
-  } else if (lj == 4) {
-    rlo = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(lo, 0x141, 0xF, 0xF, true), 0x1B,
-                                   0xF, 0xF, true);  // row_half_mirror, quad_perm [3,2,1,0]
-    rhi = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(hi, 0x141, 0xF, 0xF, true), 0x1B,
-                                   0xF, 0xF, true);
-  } else if (lj == 8) {
-    rlo = __builtin_amdgcn_mov_dpp(lo, 0x128, 0xF, 0xF, true);  // row_ror:8
-    rhi = __builtin_amdgcn_mov_dpp(hi, 0x128, 0xF, 0xF, true);
-  } else {
-    return __shfl_xor(v, lj, 64);
-  }
-  return ((unsigned long long)(unsigned)rhi << 32) | (unsigned)rlo;
+namespace {
+
+
+// The 32-bit value held by lane l ^ lj, lj in {1, 2, 4, 8}, all within a
+// 16-lane row: distances 1 and 2 are quad permutations, 4 a mirror of each
+// 8-lane half row (lane i reads i ^ 7) followed by a quad reversal (i ^ 3),
+// 8 a rotation of the row by 8.
+template <int LJ>
+__device__ __forceinline__ int row_xor(int v) {
+  static_assert(LJ == 1 || LJ == 2 || LJ == 4 || LJ == 8, "lane distance inside a DPP row");
+  if constexpr (LJ == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);
+  if constexpr (LJ == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);
+  if constexpr (LJ == 4)
+    return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true), 0x1B,
+                                    0xF, 0xF, true);
+  return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);
 }
 
-template <int E>
-__global__ void __launch_bounds__(256) select_kernel(const float* __restrict__ mass, int rows,
-                                                     int nkb, double tau,
-                                                     const double* __restrict__ taus,
-                                                     int rows_per_tau,
-                                                     int32_t* __restrict__ idx,
-                                                     int32_t* __restrict__ count) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + wave;
-  if (row >= rows) return;  // no barriers below: whole waves leave together
-  if (taus != nullptr) tau = taus[row / rows_per_tau];
-  const float* __restrict__ m = mass + (size_t)row * nkb;
+template <int LJ>
+__device__ __forceinline__ double row_xor(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const int lo = row_xor<LJ>((int)(unsigned)u), hi = row_xor<LJ>((int)(unsigned)(u >> 32));
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
 
-  unsigned long long key[E];
-#pragma unroll
-  for (int r = 0; r < E; ++r) {
-    const int e = lane * E + r;
-    unsigned long long kv = 0ull;  // padding sorts after every real key
-    if (e < nkb) {
-      unsigned bits = __float_as_uint(m[e]);
-      if (bits >> 31) bits = 0u;  // negative masses are treated as zero
-      kv = ((unsigned long long)bits << 32) | (unsigned long long)(0xFFFFFFFFu - (unsigned)e);
-    }
-    key[r] = kv;
+// The value held by lane ^ LJ: DPP inside a 16-lane row, ds_bpermute across.
+template <int LJ>
+__device__ __forceinline__ double lane_xor(double v) {
+  if constexpr (LJ <= 8) {
+    return row_xor<LJ>(v);
+  } else {
+    return __shfl_xor(v, LJ, 64);
   }
+}
+template <int LJ>
+__device__ __forceinline__ int lane_xor(int v) {
+  if constexpr (LJ <= 8) {
+    return row_xor<LJ>(v);
+  } else {
+    return __shfl_xor(v, LJ, 64);
+  }
+}
 
-  // bitonic sort, descending: in a k-block whose (e & k) == 0 the lower
-  // position keeps the larger key.  Each compare-exchange is one 64-bit
-  // compare whose outcome is flipped by the block's direction, then one
-  // select per word.  For k < E the direction depends only on r, for
-  // k >= E only on the lane (e = lane * E + r).
+// Minimum over the L lanes of a mass-map row.
+template <int L, int LJ = 1>
+__device__ __forceinline__ int row_min(int x) {
+  if constexpr (LJ < L) {
+    return row_min<L, 2 * LJ>(min(x, lane_xor<LJ>(x)));
+  } else {
+    return x;
+  }
+}
+
+// Keys are built from masses >= 0 (negative ones count as 0) and block
+// indices < 2^30; 0.0 pads positions past nkb and sorts after every key.
+__device__ __forceinline__ double make_key(float m, int j) {
+  const int bits = max((int)__float_as_uint(m), 0);
+  const unsigned long long k =
+      ((unsigned long long)(unsigned)bits << 30) | (unsigned long long)(0x3FFFFFFFu - (unsigned)j);
+  return __longlong_as_double((long long)k);
+}
+__device__ __forceinline__ float key_mass(double k) {
+  return __uint_as_float((unsigned)((unsigned long long)__double_as_longlong(k) >> 30));
+}
+__device__ __forceinline__ int key_block(double k) {
+  return (int)(0x3FFFFFFFu - ((unsigned)__double_as_longlong(k) & 0x3FFFFFFFu));
+}
+
+__device__ __forceinline__ double lane_sign(int l, int bit) { return (l & bit) == 0 ? 1.0 : -1.0; }
+
+// Cross-lane steps at lane distances LJ, LJ/2, ..., 1 of a folded stage (the
+// larger key goes to the lower position).  During a step the lane holds
+// g = t * f, f its folded key and t = +1 in the lower lane of each pair, -1
+// in the upper one, so the partner holds -t * f'; then max(g, -g') is t times
+// the key the lane keeps (max(f, f') below, min(f, f') above): two v_max_f64
+// and no compare (float64 compares issue far slower than max and min).
+// Entering a step the keys carry the step's t; leaving it they are switched
+// to the next step's t, and after the last one back to plain folded keys.
+template <int E, int LJ>
+__device__ __forceinline__ void cross_steps(double (&key)[E], int l) {
+  if constexpr (LJ >= 1) {
 #pragma unroll
-  for (int k = 2; k <= 64 * E; k <<= 1) {
-    const bool lane_desc = ((lane * E) & k) == 0;  // the direction when k >= E
+    for (int r = 0; r < E; ++r) key[r] = fmax(key[r], -lane_xor<LJ>(key[r]));
+    const double flip = lane_sign(l, LJ) * (LJ > 1 ? lane_sign(l, LJ / 2) : 1.0);
 #pragma unroll
-    for (int j = k >> 1; j >= 1; j >>= 1) {
-      if (j >= E) {
-        const int lj = j / E;
-        const bool lower = (lane & lj) == 0;
-        const bool take_max = (lower == lane_desc);  // here k > j >= E
+    for (int r = 0; r < E; ++r) key[r] *= flip;
+    cross_steps<E, LJ / 2>(key, l);
+  }
+}
+
+// The in-lane steps J, J/2, ..., 1 of stage K: registers r and r | J.  For
+// K < E the block's direction depends on r; from K = E on the keys are
+// folded and every exchange keeps the larger key at the lower position.
+template <int E, int K, int J>
+__device__ __forceinline__ void inlane_steps(double (&key)[E]) {
+  if constexpr (J >= 1) {
 #pragma unroll
-        for (int r = 0; r < E; ++r) {
-          const unsigned long long other = lane_xor64(key[r], lj);
-          const bool keep = (key[r] > other) == take_max;
-          key[r] = keep ? key[r] : other;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < E; ++r) {
-          if ((r & j) == 0) {
-            const int r2 = r | j;
-            const bool desc = k < E ? ((r & k) == 0) : lane_desc;
-            const unsigned long long a = key[r], b = key[r2];
-            const bool swap = (a < b) == desc;
-            key[r] = swap ? b : a;
-            key[r2] = swap ? a : b;
-          }
-        }
+    for (int r = 0; r < E; ++r) {
+      if ((r & J) == 0) {
+        const int r2 = r | J;
+        const bool desc = K >= E || (r & K) == 0;
+        const double hi = fmax(key[r], key[r2]), lo = fmin(key[r], key[r2]);
+        key[r] = desc ? hi : lo;
+        key[r2] = desc ? lo : hi;
       }
     }
+    inlane_steps<E, K, J / 2>(key);
+  }
+}
+
+// Bitonic stages K, 2K, ..., L*E over positions e = l * E + r (descending
+// overall).  In stage K the block containing e runs descending when
+// (e & K) == 0: for K < E that depends on r only; for K >= E on the lane
+// only, and there each lane's keys are multiplied by dir = +-1 for the
+// stage (fold holds the previous stage's dir).
+template <int E, int L, int K>
+__device__ __forceinline__ void stages(double (&key)[E], int l, double fold) {
+  if constexpr (K <= L * E) {
+    if constexpr (K >= E) {
+      const double dir = ((l * E) & K) == 0 ? 1.0 : -1.0;
+      double flip = dir * fold;
+      if constexpr (K > E) flip *= lane_sign(l, K / (2 * E));  // the first cross step's t
+#pragma unroll
+      for (int r = 0; r < E; ++r) key[r] *= flip;
+      fold = dir;
+    }
+    if constexpr (K > E) cross_steps<E, K / (2 * E)>(key, l);
+    inlane_steps<E, K, (K > E ? E : K) / 2>(key);
+    stages<E, L, 2 * K>(key, l, fold);
+  }
+}
+
+}  // namespace
+
+template <int E, int L>
+__global__ void __launch_bounds__(64) select_kernel(const float* __restrict__ mass, int rows,
+                                                    int nkb, double tau,
+                                                    const double* __restrict__ taus,
+                                                    int rows_per_tau,
+                                                    int32_t* __restrict__ idx,
+                                                    int32_t* __restrict__ count) {
+  constexpr int kRowsPerWave = 64 / L;
+  constexpr int kPad = E >= 4 ? 4 : 0;  // LDS words after each lane's run (bank spread)
+  constexpr int kRowWords = L * (E + kPad);
+  __shared__ int32_t stage[kRowsPerWave * kRowWords];
+
+  const int lane = threadIdx.x;
+  const int sub = lane / L, l = lane % L;
+  const int row = blockIdx.x * kRowsPerWave + sub;
+  const bool live = row < rows;
+  const float* __restrict__ m = mass + (size_t)(live ? row : 0) * nkb;
+
+  // register r of lane l holds block r * L + l (coalesced reads); where a
+  // key starts does not matter, it carries its own block index
+  double key[E];
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const int j = r * L + l;
+    key[r] = (live && j < nkb) ? make_key(m[j], j) : 0.0;
   }
 
-  // float64 inclusive prefix of the sorted masses
-  double pre[E];
+  // bitonic sort, descending
+  stages<E, L, 2>(key, l, 1.0);
+  // the last stage (K = P) runs descending everywhere: the keys end unfolded
+
+  if (live && taus != nullptr) tau = taus[row / rows_per_tau];
+  // prefixes are sums of masses >= +0, where doubles order like their bit
+  // patterns: compare those (a threshold <= 0 is reached at once, NaN never)
+  const unsigned long long tau_bits =
+      tau > 0.0 ? (unsigned long long)__double_as_longlong(tau) : (tau <= 0.0 ? 0ull : ~0ull);
+
+  // float64 prefix of the sorted masses: the lane's sum, an inclusive scan
+  // over the row's L lanes, then each position's prefix as the previous
+  // lanes' total plus the lane's running sum
+  double lane_total = 0.0;
+#pragma unroll
+  for (int r = 0; r < E; ++r)
+    if (l * E + r < nkb) lane_total += (double)key_mass(key[r]);
+  double incl = lane_total;
+#pragma unroll
+  for (int off = 1; off < L; off <<= 1) {
+    const double y = __shfl_up(incl, off, L);
+    if (l >= off) incl += y;
+  }
+  double excl = __shfl_up(incl, 1, L);
+  if (l == 0) excl = 0.0;
+
+  int first = nkb;  // first sorted position whose prefix reaches tau
   double run = 0.0;
 #pragma unroll
   for (int r = 0; r < E; ++r) {
-    run += (double)__uint_as_float((unsigned)(key[r] >> 32));
-    pre[r] = run;
+    const int e = l * E + r;
+    if (e < nkb) {
+      run += (double)key_mass(key[r]);
+      if ((unsigned long long)__double_as_longlong(excl + run) >= tau_bits) first = min(first, e);
+    }
   }
-  double incl = run;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  double excl = __shfl_up(incl, 1, 64);
-  if (lane == 0) excl = 0.0;
-
-  int first = nkb;  // first sorted position whose prefix reaches tau
-#pragma unroll
-  for (int r = 0; r < E; ++r) {
-    const int e = lane * E + r;
-    if (e < nkb && excl + pre[r] >= tau) first = min(first, e);
-  }
-  first = wave_min(first);
+  first = row_min<L>(first);
   const int cnt = (tau >= 1.0 || first >= nkb) ? nkb : first + 1;
 
-  int32_t* __restrict__ out = idx + (size_t)row * nkb;
+  // kept indices in sorted order, through LDS so that the global stores of
+  // a row cover L consecutive entries each
+  int32_t* st = stage + sub * kRowWords + l * (E + kPad);
 #pragma unroll
-  for (int r = 0; r < E; ++r) {
-    const int e = lane * E + r;
-    if (e < cnt) out[e] = (int32_t)(0xFFFFFFFFu - (unsigned)(key[r] & 0xFFFFFFFFull));
+  for (int r = 0; r < E; ++r) st[r] = key_block(key[r]);
+  __syncthreads();
+  if (live) {
+    int32_t* __restrict__ out = idx + (size_t)row * nkb;
+    const int32_t* rs = stage + sub * kRowWords;
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      const int e = r * L + l;
+      if (e < cnt) out[e] = rs[(e / E) * (E + kPad) + (e % E)];
+    }
+    if (l == 0) count[row] = cnt;
   }
-  if (lane == 0) count[row] = cnt;
 }
 
 hipError_t launch_select(int32_t rows, int32_t nkb, const float* mass, double tau,
                          const double* taus, int32_t rows_per_tau, int32_t* idx, int32_t* count,
                          hipStream_t stream) {
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-  if (nkb <= 64) {
-    hipLaunchKernelGGL(select_kernel<1>, grid, block, 0, stream, mass, rows, nkb, tau, taus,
-                       rows_per_tau, idx, count);
+  // P = pow2(nkb) positions: L = max(16, P / 16) lanes per row, E = P / L
+#define LOSA_SELECT(P)                                                                         \
+  do {                                                                                         \
+    constexpr int L = (P) / 16 > 16 ? (P) / 16 : 16;                                           \
+    constexpr int E = (P) / L;                                                                 \
+    const dim3 grid((unsigned)((rows + 64 / L - 1) / (64 / L))), block(64);                    \
+    hipLaunchKernelGGL((select_kernel<E, L>), grid, block, 0, stream, mass, rows, nkb, tau,    \
+                       taus, rows_per_tau, idx, count);                                        \
+  } while (0)
+  if (nkb <= 16) {
+    LOSA_SELECT(16);
+  } else if (nkb <= 32) {
+    LOSA_SELECT(32);
+  } else if (nkb <= 64) {
+    LOSA_SELECT(64);
   } else if (nkb <= 128) {
-    hipLaunchKernelGGL(select_kernel<2>, grid, block, 0, stream, mass, rows, nkb, tau, taus,
-                       rows_per_tau, idx, count);
+    LOSA_SELECT(128);
   } else if (nkb <= 256) {
-    hipLaunchKernelGGL(select_kernel<4>, grid, block, 0, stream, mass, rows, nkb, tau, taus,
-                       rows_per_tau, idx, count);
+    LOSA_SELECT(256);
   } else if (nkb <= 512) {
-    hipLaunchKernelGGL(select_kernel<8>, grid, block, 0, stream, mass, rows, nkb, tau, taus,
-                       rows_per_tau, idx, count);
+    LOSA_SELECT(512);
   } else if (nkb <= 1024) {
-    hipLaunchKernelGGL(select_kernel<16>, grid, block, 0, stream, mass, rows, nkb, tau, taus,
-                       rows_per_tau, idx, count);
+    LOSA_SELECT(1024);
   } else {
     return hipErrorInvalidValue;
   }
+#undef LOSA_SELECT
   return hipGetLastError();
 }
 

@@ -272,17 +272,24 @@ def test_select_matches_oracle_on_given_masses(losa, nkb):
     rng = np.random.default_rng(nkb)
     rows = 37
     mass = np.empty((rows, nkb), np.float32)
+    tiny = np.array([1.4e-45, 4.2e-45, 1e-40, 2.5e-39], np.float32)   # float32 denormals
     for r in range(rows):
-        kind = r % 4
+        kind = r % 5
         if kind == 0:
             x = rng.dirichlet(np.full(nkb, 0.05))
         elif kind == 1:
             x = rng.dirichlet(np.full(nkb, 5.0))
         elif kind == 2:
             x = np.full(nkb, 1.0 / nkb)          # ties everywhere
-        else:
+        elif kind == 3:
             x = rng.dirichlet(np.full(nkb, 0.5))
             x[rng.integers(0, nkb, max(1, nkb // 4))] = 0.0   # exact zeros
+        else:
+            # denormal masses, many equal, among ordinary ones (the device
+            # sorts them as denormal float64 keys)
+            x = rng.dirichlet(np.full(nkb, 0.5)).astype(np.float32)
+            pick = rng.integers(0, nkb, max(1, nkb // 3))
+            x[pick] = rng.choice(tiny, len(pick))
         mass[r] = x.astype(np.float32)
     tm = torch.from_numpy(mass).cuda()
     for tau in TAUS + (0.3, 2.0):
