@@ -34,7 +34,6 @@ namespace losa {
 
 namespace {
 
-
 // The 32-bit value held by lane l ^ lj, lj in {1, 2, 4, 8}, all within a
 // 16-lane row: distances 1 and 2 are quad permutations, 4 a mirror of each
 // 8-lane half row (lane i reads i ^ 7) followed by a quad reversal (i ^ 3),
@@ -100,6 +99,7 @@ __device__ __forceinline__ int key_block(double k) {
   return (int)(0x3FFFFFFFu - ((unsigned)__double_as_longlong(k) & 0x3FFFFFFFu));
 }
 
+// +1 in a lane whose `bit` is clear, -1 where it is set.
 __device__ __forceinline__ double lane_sign(int l, int bit) { return (l & bit) == 0 ? 1.0 : -1.0; }
 
 // Cross-lane steps at lane distances LJ, LJ/2, ..., 1 of a folded stage (the
