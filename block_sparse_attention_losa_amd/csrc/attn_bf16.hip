@@ -12,10 +12,12 @@
 //             the construction step needs one sweep over the keys, not two.
 //
 // One workgroup (4 waves) owns 128 query rows -- two 64-row query blocks or
-// one 128-row block -- and each wave owns 32 of them.  Every 64-key K/V
-// tile brought into LDS therefore feeds 128 rows, which halves the L2
-// traffic per flop compared with one 64-row block per workgroup; at 64 rows
-// the K/V feed alone would need the whole L2 bandwidth at MFMA peak.  For
+// one 128-row block -- and each wave owns 32 of them; the dense passes at
+// D = 128 use 256-row workgroups of 8 waves (one per CU).  Every 64-key K/V
+// tile brought into LDS therefore feeds 128 (or 256) rows, which halves (or
+// quarters) the L2 traffic per flop compared with one 64-row block per
+// workgroup; at 64 rows the K/V feed alone would need the whole L2
+// bandwidth at MFMA peak.  For
 // sparse attention the workgroup walks the union of its query blocks' frozen
 // lists (ascending) and each wave skips the tiles its own block did not
 // keep.  Workgroups take their work item from the XCD-aware default order
@@ -33,9 +35,10 @@
 //    dim) are free of bank conflicts;
 //  * K runs one tile ahead of V: the scores of tile t+1 are computed on the
 //    matrix cores while tile t's softmax runs on the VALU, and the loads of
-//    K(t+2) and V(t+1) are in flight during both; the score MFMAs issue at a
-//    lower wave priority than the softmax, so the two waves of a SIMD tend
-//    to alternate between the matrix core and the VALU.
+//    K(t+2) and V(t+1) are in flight during both; in 128-row workgroups the
+//    score MFMAs issue at a lower wave priority than the softmax, so the two
+//    waves of a SIMD (from different workgroups) tend to alternate between
+//    the matrix core and the VALU.
 //
 // Scores are computed transposed, S^T = K Q^T, on 32x32x16 MFMA tiles: a
 // lane then holds one query row and 16 of the 32 keys of a chunk, so row
