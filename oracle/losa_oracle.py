@@ -13,7 +13,7 @@ Notation follows the pages: ``s`` scores, ``lse`` row log-sum-exp, ``M`` the
 block mass map, ``tau`` the retained-mass threshold, ``idx``/``count`` the
 frozen per-(head, query block) key-block lists.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * softmax scale ``c = 1/sqrt(D)`` unless given;
   * a block is ``block`` consecutive tokens of the flattened sequence; the
     last block holds the ``N - (nb-1)*block`` remaining tokens;
