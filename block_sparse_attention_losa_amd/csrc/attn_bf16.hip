@@ -35,10 +35,11 @@
 //    dim) are free of bank conflicts;
 //  * K runs one tile ahead of V: the scores of tile t+1 are computed on the
 //    matrix cores while tile t's softmax runs on the VALU, and the loads of
-//    K(t+2) and V(t+1) are in flight during both; in 128-row workgroups the
-//    score MFMAs issue at a lower wave priority than the softmax, so the two
-//    waves of a SIMD (from different workgroups) tend to alternate between
-//    the matrix core and the VALU.
+//    K(t+2) and V(t+1) are in flight during both.  The D = 128 sparse pass
+//    issues those score MFMAs inside the softmax block, interleaved with the
+//    exponentials; the other 128-row passes issue them ahead of it at a
+//    lower wave priority, so the two waves of a SIMD (from different
+//    workgroups) tend to alternate between the matrix core and the VALU.
 //
 // Scores are computed transposed, S^T = K Q^T, on 32x32x16 MFMA tiles: a
 // lane then holds one query row and 16 of the 32 keys of a chunk, so row
@@ -268,8 +269,23 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
     return __builtin_bit_cast(bf16x8, wv);
   };
 
-  // softmax of tile t (scores in sc) and its P V product
-  auto consume = [&](int t, int key0, f32x16 (&sc)[2], auto masked) {
+  // Sparse at D = 128: the next tile's score MFMAs are issued inside the
+  // softmax block (after the rare raise branch), where the scheduler
+  // interleaves them with the exponentials.  That needs the softmax on every
+  // tile of the union, so a wave whose query block did not keep the tile
+  // runs it against an exponent reference of +inf -- exact zero
+  // probabilities, no raise, P V adds nothing, the same bits -- instead of
+  // branching around it.  The union exceeds each list by ~3 %; measured
+  // 0.7 % faster than the branch with the score MFMAs at a lower wave
+  // priority.  At D = 64 the softmax VALU is the bottleneck and the extra
+  // tiles made it 12 % slower.
+  constexpr bool kInline = MODE == kSparse && D == 128;
+
+  // softmax of tile t (scores in sc) and its P V product; with kInline also
+  // the scores of the next tile (K in nslot) into sn.  keep is false for a
+  // tile this wave's query block did not keep (kInline only).
+  auto consume = [&](int t, int key0, f32x16 (&sc)[2], auto masked,
+                     const unsigned char* nslot, f32x16 (&sn)[2], bool keep) {
     if constexpr (decltype(masked)::value) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
@@ -298,7 +314,7 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[cc][i]);
       mx = pair_max(mx);
-      const float m_cand = mx * c2;
+      const float m_cand = keep ? mx * c2 : -INFINITY;
       const bool raise = m_cand > m_thr;
       const bool any_raise = __ballot(raise) != 0;
       float alpha = 1.0f;
@@ -319,13 +335,15 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
             for (int i = 0; i < 16; ++i) oacc[mt][i] *= alpha;
         }
       }
+      if constexpr (kInline) compute_s(nslot, sn);
+      const float m_e = keep ? m_use : INFINITY;
       float pr[2][16];
       float lsum = 0.f;
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          pr[cc][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][i], c2, -m_use));
+          pr[cc][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][i], c2, -m_e));
           lsum += pr[cc][i];
         }
       // alpha is 1 unless the wave raised, and fma(l, 1, x) rounds exactly
@@ -396,7 +414,7 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   // from different workgroups, whose steps drift apart; in a 256-row
   // workgroup (one per CU) both are in the same workgroup, in lockstep, and
   // equal priorities are 1.3 % faster there.
-  constexpr bool kPrio = ROWS == 128;
+  constexpr bool kPrio = ROWS == 128 && !kInline;
 
   // One pipelined step.  `masked` is true only for a final tile that runs
   // past the sequence end (ascending lists put the short last block last).
@@ -439,21 +457,23 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
     // MFMAs) and the other in its score MFMAs, the softmax issues first and
     // the score MFMAs fill its stalls (measured: 1-3 % faster than equal
     // priorities).
-    if constexpr (MODE == kSparse) {
+    if constexpr (kInline) {
+      consume(t, key0, sc, masked, kslot[(t + 1) & 1], sn, ((e0 >> (16 + qi)) & 1) != 0);
+    } else if constexpr (MODE == kSparse) {
       // waves skip the softmax and P V of tiles their query block did not
       // keep; the next tile's scores are computed regardless (the union
       // exceeds each list by ~3 %), which keeps that work branch-free
       if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
       compute_s(kslot[(t + 1) & 1], sn);
       if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
-      if (((e0 >> (16 + qi)) & 1) != 0) consume(t, key0, sc, masked);
+      if (((e0 >> (16 + qi)) & 1) != 0) consume(t, key0, sc, masked, nullptr, sn, true);
     } else {
       // scores of the next tile; after the last tile this reads a stale
       // slot and the result is dropped, which keeps the block branch-free
       if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
       compute_s(kslot[(t + 1) & 1], sn);
       if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
-      consume(t, key0, sc, masked);
+      consume(t, key0, sc, masked, nullptr, sn, true);
     }
     wait_dma_all();
     __syncthreads();
@@ -476,7 +496,9 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   if (ntile > 0) {
     wait_dma_all();
     __syncthreads();
-    if (MODE != kSparse || member(0)) compute_s(kslot[0], sa);
+    // (with kInline every wave runs the softmax of tile 0, so its scores
+    // must be real numbers even where the wave's block did not keep it)
+    if (MODE != kSparse || kInline || member(0)) compute_s(kslot[0], sa);
     __syncthreads();  // K slot 0 may be refilled from here on
   }
   const bool last_short = ntile > 0 && key0_of(ntile - 1) + 64 > N;
