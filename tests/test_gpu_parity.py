@@ -266,6 +266,73 @@ def test_sparse_arbitrary_lists(losa, d, blk, dtype):
     assert (o_g[0, 1, lo:] == 0).all() and np.isneginf(lse_g[0, 1, lo:]).all()
 
 
+def _clean_lists(idx, cnt, nb):
+    """The lists as the library reads them: the first min(max(count, 0), nb)
+    entries, those outside [0, nb) dropped, each block once."""
+    out_i = np.zeros_like(idx)
+    out_c = np.zeros_like(cnt)
+    for i in range(idx.shape[0]):
+        seen = []
+        for j in idx[i, :min(max(int(cnt[i]), 0), nb)]:
+            if 0 <= j < nb and j not in seen:
+                seen.append(int(j))
+        out_i[i, :len(seen)] = seen
+        out_c[i] = len(seen)
+    return out_i, out_c
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_sparse_partner_blocks_and_list_guarantees(losa, d):
+    """Query blocks that share a workgroup (2w and 2w+1 at block 64) with
+    very different lists -- one empty beside a complete one, one holding only
+    the short last block -- and lists with repeated entries, entries outside
+    [0, nb) and counts below 0 or above nb, which the library reads as the
+    set of in-range entries among the first count (clamped) entries.  Planned
+    and unplanned calls give the same bits."""
+    cfg = synth.small_config(n_grid=(4, 8, 15), head_dim=d, block=64, heads=2,
+                             alpha=(2.0, 0.5), seed=23)
+    _say(f"[parity] partner blocks and list guarantees d={d}")
+    q, k, v = synth.make_inputs(cfg)
+    nb = cfg.num_blocks
+    assert nb == 8 and cfg.seq_len == 480    # last block holds 32 tokens
+    rng = np.random.default_rng(9)
+    idx = np.zeros((1, 2, nb, nb), np.int32)
+    cnt = np.zeros((1, 2, nb), np.int32)
+    idx[0, 0, 0], cnt[0, 0, 0] = rng.permutation(nb), 0          # empty beside ...
+    idx[0, 0, 1], cnt[0, 0, 1] = np.arange(nb)[::-1], nb         # ... a complete list
+    idx[0, 0, 2, 0], cnt[0, 0, 2] = nb - 1, 1                    # the short last block only
+    idx[0, 0, 3], cnt[0, 0, 3] = rng.permutation(nb), nb
+    idx[0, 0, 4, :6], cnt[0, 0, 4] = [3, 3, 5, 5, 5, 3], 6       # repeats
+    idx[0, 0, 5, :6], cnt[0, 0, 5] = [-1, 2, nb, 100, 4, -7], 6  # outside [0, nb)
+    idx[0, 0, 6], cnt[0, 0, 6] = rng.permutation(nb), nb + 5     # count above nb
+    idx[0, 0, 7], cnt[0, 0, 7] = rng.permutation(nb), -3         # count below 0
+    for i in range(nb):
+        idx[0, 1, i] = rng.permutation(nb)
+        cnt[0, 1, i] = rng.integers(0, nb + 1)
+    cnt[0, 1, 2] = 0
+    cnt[0, 1, 3] = nb
+    tq, tk, tv = (_dev(x, "bf16") for x in (q, k, v))
+    ti, tc = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    o, lse = losa.sparse_attn(tq, tk, tv, ti, tc, block=64, want_lse=True)
+    plan = losa.sparse_plan(tc, block=64, head_dim=d)
+    o2, lse2 = losa.sparse_attn(tq, tk, tv, ti, tc, block=64, want_lse=True, plan=plan)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    o_g, lse_g = _np(o), _np(lse)
+    for h in range(2):
+        ci, cc = _clean_lists(idx[0, h], cnt[0, h], nb)
+        qbs = [i for i in range(nb) if cc[i] > 0]
+        ref_o, ref_lse = oracle.sparse_attention(q[0, h], k[0, h], v[0, h], ci, cc, 64,
+                                                 qblocks=qbs)
+        rows = np.concatenate([np.arange(i * 64, min(cfg.seq_len, (i + 1) * 64)) for i in qbs])
+        _compare_attention(o_g[0, h, rows], lse_g[0, h, rows], ref_o, ref_lse,
+                           f"partner lists d={d} h{h}")
+        for i in range(nb):
+            if cc[i] == 0:
+                r = slice(i * 64, min(cfg.seq_len, (i + 1) * 64))
+                assert (o_g[0, h, r] == 0).all() and np.isneginf(lse_g[0, h, r]).all(), (h, i)
+
+
 @pytest.mark.parametrize("nkb", [1, 3, 16, 64, 65, 200, 512, 929, 1024])
 def test_select_matches_oracle_on_given_masses(losa, nkb):
     _say(f"[parity] select nkb={nkb}")
