@@ -196,7 +196,7 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   float m_use = 0.f;        // m_run, or 0 while it is -inf (no finite score yet)
   float l_run = 0.f;        // this lane's partial row sum
   const float c2 = p.scale * kLog2e;
-  float lse_row = 0.f;      // kMass: the row's lse (natural), +inf on padding rows
+  float lse_row = 0.f;      // kMass: the row's lse in log2 units, +inf on padding rows
   float tacc = 0.f;         // kDenseMass: current key block's share of the row sum
   float m0 = 0.f;           // kDenseMass: reference of the first key block
   float pend = 0.f;         // kDenseMass: finished block sum not yet stored ...
@@ -209,7 +209,12 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
       }
     }
   };
-  if constexpr (MODE == kMass) lse_row = row_ok ? p.lse_in[(size_t)bh * N + row] : INFINITY;
+  // kMass takes exp2(s c log2(e) - lse log2(e)) as one fma and an exp2: the
+  // exponent carries the roundings of c log2(e) (times the logit) and of
+  // lse log2(e), each <= 2^-24 relative, ~1e-5 for logits near 100 (the
+  // softmax that produced lse saw the same c log2(e)); measured 7-8 % faster
+  // than fma(s, c, -lse) * log2(e), masses within 7e-7 of it
+  if constexpr (MODE == kMass) lse_row = row_ok ? p.lse_in[(size_t)bh * N + row] * kLog2e : INFINITY;
 
   // S^T of this wave's 32 rows against both 32-key chunks of the K tile
   const int prow = perm_row(l32);
@@ -299,7 +304,7 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][i], p.scale, -lse_row) * kLog2e);
+          acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][i], c2, -lse_row));
       acc = wave_sum(acc);
       if (lane == 0) part[wave * G::kMaxBlocks + (key0 / BLK)] += acc;
     } else {
