@@ -418,7 +418,8 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   // Wave priorities (below) pay off when the two waves sharing a SIMD come
   // from different workgroups, whose steps drift apart; in a 256-row
   // workgroup (one per CU) both are in the same workgroup, in lockstep, and
-  // equal priorities are 1.3 % faster there.
+  // equal priorities are 1.3 % faster there.  With kInline the score MFMAs
+  // share the softmax block, so there is no separate phase to rank.
   constexpr bool kPrio = ROWS == 128 && !kInline;
 
   // One pipelined step.  `masked` is true only for a final tile that runs
@@ -455,7 +456,7 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
       if (t + 1 < ntile)
         dma_tile(vh, kHave ? key0_from(e1, t + 1) : key0_of(t + 1),
                  vslot[(t + 1) & 1], voff);
-    // Wave priority (128-row workgroups): the next tile's score MFMAs issue
+    // Wave priority (kPrio): the next tile's score MFMAs issue
     // at the lowest level, everything else (softmax, P V, loads, the
     // barrier) one above.  The two waves sharing a SIMD come from different
     // workgroups; when one is in its softmax (the critical path to its P V
