@@ -18,6 +18,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,7 +31,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_wan13_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_attention_losa_amd", "csrc", f)
-                  for f in ("attn_bf16.hip", "attn_common.h", "losa_device.h")]
+                  for f in ("attn_bf16.hip", "attn_common.h", "losa_device.h",
+                            "losa_launch.h", "frozen_lists.hip")]
 
 
 def log(msg):
@@ -38,12 +40,16 @@ def log(msg):
 
 
 def kernel_hash():
-    """Hash of the sources of the timed kernel (identifies the build a
-    counter summary was taken on)."""
+    """Hash of the code of the timed kernel, its launch shapes and its launch
+    plan (identifies the build a counter summary was taken on).  Comments
+    and whitespace are left out, so editing a comment keeps the summary."""
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as fh:
-            h.update(fh.read())
+        with open(path, encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
