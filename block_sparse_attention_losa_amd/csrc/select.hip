@@ -28,33 +28,12 @@
 // sequential accumulation.  The threshold is one value for every row, or
 // (per-row variant) taus[row / rows_per_tau].
 #include "losa_device.h"
+#include "losa_dpp.h"
 #include "losa_launch.h"
 
 namespace losa {
 
 namespace {
-
-// The 32-bit value held by lane l ^ lj, lj in {1, 2, 4, 8}, all within a
-// 16-lane row: distances 1 and 2 are quad permutations, 4 a mirror of each
-// 8-lane half row (lane i reads i ^ 7) followed by a quad reversal (i ^ 3),
-// 8 a rotation of the row by 8.
-template <int LJ>
-__device__ __forceinline__ int row_xor(int v) {
-  static_assert(LJ == 1 || LJ == 2 || LJ == 4 || LJ == 8, "lane distance inside a DPP row");
-  if constexpr (LJ == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);
-  if constexpr (LJ == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);
-  if constexpr (LJ == 4)
-    return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true), 0x1B,
-                                    0xF, 0xF, true);
-  return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);
-}
-
-template <int LJ>
-__device__ __forceinline__ double row_xor(double v) {
-  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-  const int lo = row_xor<LJ>((int)(unsigned)u), hi = row_xor<LJ>((int)(unsigned)(u >> 32));
-  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
-}
 
 // The value held by lane ^ LJ: DPP inside a 16-lane row, ds_bpermute across.
 template <int LJ>
