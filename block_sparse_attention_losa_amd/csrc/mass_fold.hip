@@ -16,7 +16,6 @@
 // HBM-bound: every stored value is read once (4 bytes per row and key
 // block) and one fp32 mass is written per (query block, key block).
 #include "losa_device.h"
-#include "losa_dpp.h"
 #include "losa_launch.h"
 
 namespace losa {

@@ -28,7 +28,6 @@
 // sequential accumulation.  The threshold is one value for every row, or
 // (per-row variant) taus[row / rows_per_tau].
 #include "losa_device.h"
-#include "losa_dpp.h"
 #include "losa_launch.h"
 
 namespace losa {
