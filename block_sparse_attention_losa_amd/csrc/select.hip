@@ -52,6 +52,32 @@ __device__ __forceinline__ int lane_xor(int v) {
   }
 }
 
+// A DPP move of a double (both halves), 0 in lanes the control leaves
+// without a source or whose row is not in ROWMASK.
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, ROWMASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, ROWMASK, 0xF,
+                                             false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
+// Inclusive prefix sum over the L lanes of a mass-map row, all in DPP: a
+// Hillis-Steele scan inside each 16-lane row (row_shr 1, 2, 4, 8), then for
+// L >= 32 the last lane of rows 0 and 2 added to rows 1 and 3 (row_bcast:15)
+// and for L = 64 lane 31 added to rows 2 and 3 (row_bcast:31).
+template <int L>
+__device__ __forceinline__ double row_scan(double x) {
+  x += dpp_f64<0x111>(x);
+  x += dpp_f64<0x112>(x);
+  x += dpp_f64<0x114>(x);
+  x += dpp_f64<0x118>(x);
+  if constexpr (L >= 32) x += dpp_f64<0x142, 0xA>(x);
+  if constexpr (L == 64) x += dpp_f64<0x143, 0xC>(x);
+  return x;
+}
+
 // Minimum over the L lanes of a mass-map row.
 template <int L, int LJ = 1>
 __device__ __forceinline__ int row_min(int x) {
@@ -188,13 +214,10 @@ __global__ void __launch_bounds__(64) select_kernel(const float* __restrict__ ma
 #pragma unroll
   for (int r = 0; r < E; ++r)
     if (l * E + r < nkb) lane_total += (double)key_mass(key[r]);
-  double incl = lane_total;
-#pragma unroll
-  for (int off = 1; off < L; off <<= 1) {
-    const double y = __shfl_up(incl, off, L);
-    if (l >= off) incl += y;
-  }
-  double excl = __shfl_up(incl, 1, L);
+  const double incl = row_scan<L>(lane_total);
+  // the previous lane's prefix: row_shr:1 inside a 16-lane row, wave_shr:1
+  // across rows (which hands lane 0 of the next mass-map row a value too)
+  double excl = L == 16 ? dpp_f64<0x111>(incl) : dpp_f64<0x138>(incl);
   if (l == 0) excl = 0.0;
 
   int first = nkb;  // first sorted position whose prefix reaches tau
