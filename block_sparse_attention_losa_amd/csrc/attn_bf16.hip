@@ -36,10 +36,11 @@
 //  * K runs one tile ahead of V: the scores of tile t+1 are computed on the
 //    matrix cores while tile t's softmax runs on the VALU, and the loads of
 //    K(t+2) and V(t+1) are in flight during both.  The D = 128 sparse pass
-//    issues those score MFMAs inside the softmax block, interleaved with the
-//    exponentials; the other 128-row passes issue them ahead of it at a
-//    lower wave priority, so the two waves of a SIMD (from different
-//    workgroups) tend to alternate between the matrix core and the VALU.
+//    and the mass pass issue those score MFMAs inside the softmax block,
+//    interleaved with the exponentials; the other 128-row passes issue them
+//    ahead of it at a lower wave priority, so the two waves of a SIMD (from
+//    different workgroups) tend to alternate between the matrix core and
+//    the VALU.
 //
 // Scores are computed transposed, S^T = K Q^T, on 32x32x16 MFMA tiles: a
 // lane then holds one query row and 16 of the 32 keys of a chunk, so row
@@ -283,8 +284,9 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   // branching around it.  The union exceeds each list by ~3 %; measured
   // 0.7 % faster than the branch with the score MFMAs at a lower wave
   // priority.  At D = 64 the softmax VALU is the bottleneck and the extra
-  // tiles made it 12 % slower.
-  constexpr bool kInline = MODE == kSparse && D == 128;
+  // tiles made it 12 % slower.  The mass pass (no P V, every wave keeps
+  // every tile) issues them the same way: 1-2 % faster, the same bits.
+  constexpr bool kInline = (MODE == kSparse && D == 128) || MODE == kMass;
 
   // softmax of tile t (scores in sc) and its P V product; with kInline also
   // the scores of the next tile (K in nslot) into sn.  keep is false for a
@@ -299,6 +301,7 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
           if (key0 + cc * 32 + perm_row(c_row(i, g)) >= N) sc[cc][i] = -INFINITY;
     }
     if constexpr (MODE == kMass) {
+      compute_s(nslot, sn);
       float acc = 0.f;
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
@@ -463,7 +466,9 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
     // MFMAs) and the other in its score MFMAs, the softmax issues first and
     // the score MFMAs fill its stalls (measured: 1-3 % faster than equal
     // priorities).
-    if constexpr (kInline) {
+    if constexpr (kInline && MODE == kMass) {
+      consume(t, key0, sc, masked, kslot[(t + 1) & 1], sn, true);
+    } else if constexpr (kInline) {
       consume(t, key0, sc, masked, kslot[(t + 1) & 1], sn, ((e0 >> (16 + qi)) & 1) != 0);
     } else if constexpr (MODE == kSparse) {
       // waves skip the softmax and P V of tiles their query block did not
