@@ -35,8 +35,9 @@
 //    dim) are free of bank conflicts;
 //  * K runs one tile ahead of V: the scores of tile t+1 are computed on the
 //    matrix cores while tile t's softmax runs on the VALU, and the loads of
-//    K(t+2) and V(t+1) are in flight during both.  The D = 128 sparse pass
-//    and the mass pass issue those score MFMAs inside the softmax block,
+//    K(t+2) and V(t+1) are in flight during both.  The D = 128 sparse pass,
+//    the mass pass and the D = 64 dense pass issue those score MFMAs inside
+//    the softmax block,
 //    interleaved with the exponentials; the other 128-row passes issue them
 //    ahead of it at a lower wave priority, so the two waves of a SIMD (from
 //    different workgroups) tend to alternate between the matrix core and
@@ -285,8 +286,11 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   // 0.7 % faster than the branch with the score MFMAs at a lower wave
   // priority.  At D = 64 the softmax VALU is the bottleneck and the extra
   // tiles made it 12 % slower.  The mass pass (no P V, every wave keeps
-  // every tile) issues them the same way: 1-2 % faster, the same bits.
-  constexpr bool kInline = (MODE == kSparse && D == 128) || MODE == kMass;
+  // every tile) and the D = 64 dense pass (128-row workgroups) issue them
+  // the same way: 1-2 % faster, the same bits.  (The 256-row dense passes
+  // measured within noise, the D = 64 dense+mass pass 9 % slower.)
+  constexpr bool kInline =
+      (MODE == kSparse && D == 128) || MODE == kMass || (MODE == kDense && D == 64);
 
   // softmax of tile t (scores in sc) and its P V product; with kInline also
   // the scores of the next tile (K in nslot) into sn.  keep is false for a
@@ -466,7 +470,7 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
     // MFMAs) and the other in its score MFMAs, the softmax issues first and
     // the score MFMAs fill its stalls (measured: 1-3 % faster than equal
     // priorities).
-    if constexpr (kInline && MODE == kMass) {
+    if constexpr (kInline && MODE != kSparse) {
       consume(t, key0, sc, masked, kslot[(t + 1) & 1], sn, true);
     } else if constexpr (kInline) {
       consume(t, key0, sc, masked, kslot[(t + 1) & 1], sn, ((e0 >> (16 + qi)) & 1) != 0);
