@@ -1,0 +1,46 @@
+"""Host-side logic of bench.py: the one-GPU guard, the kernel-source hash
+that ties a committed counter summary to the code it was taken on, and the
+algorithmic work it reports (4*|I|*|J|*D flop per kept block pair)."""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_kernel_hash_follows_code_not_comments(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(src)])
+    src.write_text("int f(int x) { return x + 1; }\n")
+    h0 = bench.kernel_hash()
+    src.write_text("// a comment\nint f(int x)   {\n  /* block\n comment */ return x + 1;  // tail\n}\n")
+    assert bench.kernel_hash() == h0
+    src.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.kernel_hash() != h0
+
+
+def test_kept_flops_counts_ragged_blocks():
+    # N = 100 tokens, block 64: blocks of 64 and 36 tokens; D = 8
+    count = np.array([[[1, 2]]], np.int32)
+    idx = np.array([[[[1, 0], [0, 1]]]], np.int32)
+    # (I0, J1) 64*36, (I1, J0) 36*64, (I1, J1) 36*36
+    expect = 4.0 * (64 * 36 + 36 * 64 + 36 * 36) * 8
+    assert bench.kept_flops(count, idx, 100, 64, 8) == expect
+    # every pair kept: the dense count
+    full = np.array([[[2, 2]]], np.int32)
+    both = np.array([[[[0, 1], [0, 1]]]], np.int32)
+    assert bench.kept_flops(full, both, 100, 64, 8) == bench.dense_flops(1, 1, 100, 8)
