@@ -1,9 +1,14 @@
 """GPU parity of the functions over the frozen lists: per-row thresholds,
 the block mask and the retained-mass (drift) diagnostic, against the oracle.
 
-Tolerances: selection and masks bit-identical; retained mass 2e-3 absolute
-(it is exp(lse' - lse) of two fp32 log-sum-exps, each within 1e-3 of the
-oracle's; their errors largely cancel, and measured gaps are ~1e-5).
+Tolerances: selection and masks bit-identical.  The retained mass is
+mean_i exp(lse'_i - lse_i) of two fp32 log-sum-exps that the sparse and
+dense kernels produce; with those off the oracle's by e'_i and e_i, and
+every term at most 1, the kernel's result can be off by at most
+max_i (|e'_i| + |e_i|) over the query block's rows, plus its own fp32
+rounding (exp within 2 ulp, a sum of at most 128 terms of depth 8: below
+8e-6).  The test measures e' and e on every row and asserts that bound, so
+the drift diagnostic may add no error of its own beyond fp32 rounding.
 """
 
 import sys
@@ -14,10 +19,11 @@ import torch
 
 import oracle
 from block_sparse_attention_losa_amd import synth
+from tests import _margins
 
 pytestmark = pytest.mark.gpu
 
-RETAINED_ATOL = 2e-3
+RETAINED_FP32 = 8e-6
 
 
 def _say(msg):
@@ -121,13 +127,20 @@ CASES = {
 }
 
 
+def _retained_bound(lse_k, lse_d, ref_k, ref_d, nb, block, n):
+    """Per query block: max over its rows of |e'| + |e|, plus fp32 rounding."""
+    e = np.abs(lse_k.astype(np.float64) - ref_k) + np.abs(lse_d.astype(np.float64) - ref_d)
+    return np.array([e[i * block:min(n, (i + 1) * block)].max() for i in range(nb)]) + \
+        RETAINED_FP32
+
+
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_retained_mass_matches_oracle(losa, name):
     cfg = CASES[name]
     _say(f"[frozen] retained mass {name}")
     q, k, v = synth.make_inputs(cfg)
     tq, tk, tv = (torch.from_numpy(x).cuda().to(torch.bfloat16) for x in (q, k, v))
-    blk, nb = cfg.block, cfg.num_blocks
+    blk, nb, n = cfg.block, cfg.num_blocks, cfg.seq_len
     _, lse = losa.dense_attn(tq, tk, tv, block=blk)
     mass = losa.block_mass(tq, tk, block=blk, lse=lse)
     idx, cnt = losa.select(mass, 0.9)
@@ -141,13 +154,25 @@ def test_retained_mass_matches_oracle(losa, name):
     r9 = losa.retained_mass(lse_k, lse_d, block=blk, head_dim=cfg.head_dim)
     torch.cuda.synchronize()
     r0g, r9g = r0.cpu().numpy(), r9.cpu().numpy()
-    assert (r0g >= 0.9 - RETAINED_ATOL).all()
     ig, cg = idx.cpu().numpy(), cnt.cpu().numpy()
-    ph, pkh = (x.float().cpu().numpy() for x in (pq, pk))
+    g = {key: t.cpu().numpy() for key, t in
+         (("lse", lse), ("lse_s", lse_s), ("lse_d", lse_d), ("lse_k", lse_k))}
+    ph, pkh, pvh = (x.float().cpu().numpy() for x in (pq, pk, pv))
+    worst, tol_min = 0.0, 1.0
     for b in range(cfg.batch):
         for h in range(cfg.heads):
-            ref0 = oracle.retained_mass(q[b, h], k[b, h], ig[b, h], cg[b, h], blk)
-            ref9 = oracle.retained_mass(ph[b, h], pkh[b, h], ig[b, h], cg[b, h], blk)
-            assert np.abs(r0g[b, h] - ref0).max() <= RETAINED_ATOL, (b, h)
-            assert np.abs(r9g[b, h] - ref9).max() <= RETAINED_ATOL, (b, h)
+            for (qq, kk, vv, gk, gd, rg) in ((q, k, v, "lse_s", "lse", r0g),
+                                             (ph, pkh, pvh, "lse_k", "lse_d", r9g)):
+                ref_d = oracle.row_lse(qq[b, h], kk[b, h])
+                _, ref_k = oracle.sparse_attention(qq[b, h], kk[b, h], vv[b, h], ig[b, h],
+                                                   cg[b, h], blk)
+                ref = oracle.retained_mass(qq[b, h], kk[b, h], ig[b, h], cg[b, h], blk,
+                                           lse=ref_d)
+                tol = _retained_bound(g[gk][b, h], g[gd][b, h], ref_k, ref_d, nb, blk, n)
+                err = np.abs(rg[b, h] - ref)
+                assert (err <= tol).all(), (name, b, h, err.max(), tol.min())
+                worst, tol_min = max(worst, float(err.max())), min(tol_min, float(tol.min()))
+                if rg is r0g:
+                    assert (rg[b, h] >= 0.9 - tol).all(), (b, h)
     assert r9g.shape == (cfg.batch, cfg.heads, nb)
+    _margins.record("frozen", name, retained=worst, retained_tol_min=tol_min)

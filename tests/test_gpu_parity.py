@@ -22,6 +22,7 @@ import torch
 
 import oracle
 from block_sparse_attention_losa_amd import synth
+from tests import _margins
 
 pytestmark = pytest.mark.gpu
 
@@ -100,12 +101,29 @@ def _check_plan(plan, count, blk):
 
 
 def _compare_attention(o_gpu, lse_gpu, o_ref, lse_ref, what):
+    """Asserts the parity bounds; returns (max-abs, mean-abs, lse error)."""
     err = np.abs(o_gpu.astype(np.float64) - o_ref)
     assert err.max() <= O_MAX, f"{what}: max-abs {err.max():.3e}"
     assert err.mean() <= O_MEAN, f"{what}: mean-abs {err.mean():.3e}"
+    lerr = 0.0
     if lse_gpu is not None:
         lerr = np.abs(lse_gpu.astype(np.float64) - lse_ref).max()
         assert lerr <= LSE_ATOL, f"{what}: lse err {lerr:.3e}"
+    return float(err.max()), float(err.mean()), float(lerr)
+
+
+class _Worst:
+    """Largest error seen per quantity, for the parity-margin record."""
+
+    def __init__(self):
+        self.v = {}
+
+    def add(self, prefix, errs):
+        for key, val in zip(("o_max", "o_mean", "lse"), errs):
+            self.v[prefix + key] = max(self.v.get(prefix + key, 0.0), val)
+
+    def put(self, key, val):
+        self.v[key] = max(self.v.get(key, 0.0), float(val))
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
@@ -133,15 +151,19 @@ def test_pipeline_matches_oracle(losa, name):
     mass_fg = _np(mass_f)
     assert np.abs(mass_fg - mass_g).max() <= MASS_ATOL
 
+    worst = _Worst()
     for b in range(cfg.batch):
         for h in range(cfg.heads):
             od, lsed = oracle.dense_attention(q[b, h], k[b, h], v[b, h])
-            _compare_attention(o_g[b, h], lse_g[b, h], od, lsed, f"{name} dense b{b}h{h}")
+            worst.add("dense_", _compare_attention(o_g[b, h], lse_g[b, h], od, lsed,
+                                                   f"{name} dense b{b}h{h}"))
             md = oracle.block_mass(q[b, h], k[b, h], blk, lse=lsed)
             merr = np.abs(mass_g[b, h].astype(np.float64) - md).max()
             assert merr <= MASS_ATOL, f"{name} mass b{b}h{h} err {merr:.3e}"
             ferr = np.abs(mass_fg[b, h].astype(np.float64) - md).max()
             assert ferr <= MASS_ATOL, f"{name} one-sweep mass b{b}h{h} err {ferr:.3e}"
+            worst.put("mass", merr)
+            worst.put("mass_one_sweep", ferr)
 
     for tau in TAUS:
         _say(f"[parity] {name}: select tau={tau}")
@@ -165,13 +187,15 @@ def test_pipeline_matches_oracle(losa, name):
                         f"{name} idx tau={tau} b{b}h{h} row {i}"
                 ref_o, ref_lse = oracle.sparse_attention(q[b, h], k[b, h], v[b, h],
                                                          idx_g[b, h], cnt_g[b, h], blk)
-                _compare_attention(os_g[b, h], lses_g[b, h], ref_o, ref_lse,
-                                   f"{name} sparse tau={tau} b{b}h{h}")
+                worst.add("sparse_", _compare_attention(os_g[b, h], lses_g[b, h], ref_o,
+                                                        ref_lse,
+                                                        f"{name} sparse tau={tau} b{b}h{h}"))
         if tau == 1.0:
             # every block kept, visited in the same ascending order as the
             # dense pass: the two kernels do identical arithmetic
             assert (cnt_g == nb).all()
             assert np.array_equal(os_g, o_g) and np.array_equal(lses_g, lse_g)
+    _margins.record("parity", name, **worst.v)
 
 
 def test_repeat_runs_are_bitwise_identical(losa):

@@ -18,8 +18,13 @@ MUTANTS = {
         "s = c * (k[r] @ q.T)\n        o[a",
         [lambda: pins.test_dense_matches_brute_force(7, 3)]),
     "missing scale": (
+        "        return 1.0 / math.sqrt(d)",
+        "        return 1.0",
+        [lambda: pins.test_dense_matches_brute_force(7, 3),
+         lambda: pins.test_dense_matches_torch_sdpa_fp64()]),
+    "lse off by a constant": (
         "    lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))\n    p = np.exp(s - lse[:, None])\n    return p @ v, lse",
-        "    lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))\n    p = np.exp(s - lse[:, None])\n    return p @ v, lse + 0.0 * m + 1e-3",
+        "    lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))\n    p = np.exp(s - lse[:, None])\n    return p @ v, lse + 1e-3",
         [lambda: pins.test_dense_matches_brute_force(7, 3)]),
     "mass averaged over the full block": (
         "sum(axis=(0, 2)) / (hi - lo)",
