@@ -21,10 +21,12 @@ STATUS_NAMES = {
     6: "LOSA_ERR_DEVICE",
     7: "LOSA_ERR_BAD_ARGUMENT",
     8: "LOSA_ERR_WORKSPACE",
+    9: "LOSA_ERR_SCRATCH_LIMIT",
 }
 LOSA_BF16 = 0
 LOSA_FP32 = 1
 MAX_BLOCKS = 1024
+NOALLOC_MAX_ROWS = 4194304
 
 
 class LosaLibraryMissing(RuntimeError):
@@ -64,6 +66,7 @@ SIGNATURES = {
     "losa_num_blocks": (ctypes.c_int32, [_DESC]),
     "losa_dense_attn": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP, _VP, _VP]),
     "losa_block_mass": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "losa_block_mass_noalloc": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP]),
     "losa_dense_attn_mass_workspace": (ctypes.c_int64, [_DESC]),
     "losa_dense_attn_mass": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                             ctypes.c_int64, _VP]),

@@ -124,6 +124,26 @@ def block_mass(q, k, block: int = 64, lse=None, scale=None, mass=None, lse_scrat
     return mass
 
 
+def block_mass_noalloc(q, k, block: int = 64, scale=None, mass=None):
+    """Two-pass block mass map whose first pass keeps its lse in the
+    library's static scratch, so the library allocates no device memory
+    (pass ``mass`` to allocate nothing here either).  B*H*N must not exceed
+    ``NOALLOC_MAX_ROWS``; calls overlapping on one GPU race on the scratch."""
+    _check_inputs(mass, strided=(q, k))
+    if k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("q, k must share shape and dtype")
+    desc = make_desc(q, block, scale, k)
+    b, h, n, _ = q.shape
+    nb = num_blocks(n, block)
+    _check_out(mass, (b, h, nb, nb), torch.float32, "mass")
+    if mass is None:
+        mass = torch.empty((b, h, nb, nb), dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    _lib.check("losa_block_mass_noalloc", lib.losa_block_mass_noalloc(
+        desc, _ptr(q), _ptr(k), _ptr(mass), _stream(q)))
+    return mass
+
+
 def dense_attn_mass_workspace_bytes(q, block: int = 64) -> int:
     """Workspace bytes :func:`dense_attn_mass` needs for inputs shaped like q."""
     n = _lib.load().losa_dense_attn_mass_workspace(make_desc(q, block))

@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "liblosa.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
 HIP_SOURCES = ["attn_bf16.hip", "attn_fwd.hip", "select.hip", "mass_fold.hip",
-               "frozen_lists.hip"]
+               "frozen_lists.hip", "noalloc.hip"]
 HOST_SOURCES = ["losa_api.cpp"]
 
 ARCH = "gfx950"

@@ -37,6 +37,10 @@ bool disjoint(const losa_attn_desc* d, int64_t sb, int64_t sh, int64_t sn) {
   return true;
 }
 
+}  // namespace
+
+namespace losa {
+
 losa_status check_desc(const losa_attn_desc* d, int32_t* nb_out) {
   if (d == nullptr) return LOSA_ERR_NULL_POINTER;
   if (d->dtype != LOSA_BF16 && d->dtype != LOSA_FP32) return LOSA_ERR_BAD_DTYPE;
@@ -69,6 +73,12 @@ losa_status check_desc(const losa_attn_desc* d, int32_t* nb_out) {
   *nb_out = static_cast<int32_t>(nb);
   return LOSA_OK;
 }
+
+}  // namespace losa
+
+namespace {
+
+using losa::check_desc;
 
 float effective_scale(const losa_attn_desc* d) {
   return d->scale > 0.f ? d->scale : 1.0f / std::sqrt(static_cast<float>(d->head_dim));
@@ -351,6 +361,8 @@ const char* losa_status_string(losa_status status) {
       return "invalid argument (scale not finite or negative, bad strides or aliasing output "
              "layout, or rows per threshold < 1)";
     case LOSA_ERR_WORKSPACE: return "workspace smaller than the size the library asks for";
+    case LOSA_ERR_SCRATCH_LIMIT:
+      return "B*H*N exceeds the library's static scratch (LOSA_NOALLOC_MAX_ROWS rows)";
   }
   return "unknown status";
 }

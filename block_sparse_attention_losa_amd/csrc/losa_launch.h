@@ -6,7 +6,13 @@
 
 #include <atomic>
 
+#include "../../include/losa.h"
+
 namespace losa {
+
+// Validation of a descriptor shared by the entry points (losa_api.cpp):
+// LOSA_OK and *nb_out = ceil(N / block), or the status to return.
+losa_status check_desc(const losa_attn_desc* d, int32_t* nb_out);
 
 // kDenseMass: the dense pass that also writes, per row and key block, the
 // block's share of the row's softmax sum (see attn_bf16.hip) for the mass map.

@@ -24,7 +24,8 @@
  *    library never allocates, frees or synchronises and may be called from
  *    several host threads at once.  Its only state is set once per kernel
  *    and device on first use: the kernel's dynamic-LDS limit
- *    (hipFuncSetAttribute).  Outputs must not overlap inputs.
+ *    (hipFuncSetAttribute), and for losa_block_mass_noalloc the address of
+ *    its scratch array.  Outputs must not overlap inputs.
  *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
  *    Work is enqueued asynchronously on it, as kernel launches only (no
  *    memset or copy), so calls on different streams may run concurrently
@@ -58,7 +59,8 @@ typedef enum {
   LOSA_ERR_MISALIGNED = 5,     /* pointer alignment below the requirement   */
   LOSA_ERR_DEVICE = 6,         /* the HIP runtime rejected a launch         */
   LOSA_ERR_BAD_ARGUMENT = 7,   /* other invalid argument (e.g. scale)       */
-  LOSA_ERR_WORKSPACE = 8       /* workspace smaller than required           */
+  LOSA_ERR_WORKSPACE = 8,      /* workspace smaller than required           */
+  LOSA_ERR_SCRATCH_LIMIT = 9   /* B*H*N above LOSA_NOALLOC_MAX_ROWS          */
 } losa_status;
 
 typedef enum { LOSA_BF16 = 0, LOSA_FP32 = 1 } losa_dtype;
@@ -119,6 +121,24 @@ losa_status losa_dense_attn(const losa_attn_desc* desc, const void* q, const voi
 losa_status losa_block_mass(const losa_attn_desc* desc, const void* q, const void* k,
                             const float* lse, float* lse_scratch, float* mass,
                             void* stream);
+
+/*
+ * losa_block_mass with lse = NULL, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The first pass's row log-sum-exp goes to a scratch
+ * array of LOSA_NOALLOC_MAX_ROWS floats (16 MiB) that the library keeps in
+ * each GPU's memory for the life of the process; the call allocates and
+ * frees nothing.  Requires B*H*N <= LOSA_NOALLOC_MAX_ROWS, else
+ * LOSA_ERR_SCRATCH_LIMIT (nothing launched).  The scratch is shared by every
+ * call on a GPU: calls that overlap on one GPU (different streams or host
+ * threads) race on it and must be ordered by the caller.  The first call on
+ * a device looks the array's address up (hipGetSymbolAddress); make one call
+ * before capturing it into a graph.  mass: output [B,H,nb,nb] fp32, the
+ * same bits as losa_block_mass.
+ */
+#define LOSA_NOALLOC_MAX_ROWS 4194304
+losa_status losa_block_mass_noalloc(const losa_attn_desc* desc, const void* q, const void* k,
+                                    float* mass, void* stream);
 
 /*
  * The construction step in one sweep over the keys: dense attention (as

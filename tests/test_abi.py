@@ -46,7 +46,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in range(9):
+    for code in range(10):
         assert lib.losa_status_string(code) != b"unknown status"
     assert lib.losa_status_string(99) == b"unknown status"
     assert lib.losa_version() >= 100
@@ -203,3 +203,15 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(_lib.LosaLibraryMissing):
         _lib.load(str(tmp_path / "missing.so"))
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """The no-allocation mass entry takes B*H*N <= LOSA_NOALLOC_MAX_ROWS and
+    refuses larger inputs on the host, before touching the device."""
+    assert _lib.NOALLOC_MAX_ROWS == 4194304
+    big = desc(batch=1, heads=65, seq_len=65536, head_dim=64, block=64)   # 4 259 840 rows
+    assert lib.losa_block_mass_noalloc(big, FAKE, FAKE, FAKE, NULL) == 9
+    assert lib.losa_block_mass_noalloc(desc(head_dim=96), FAKE, FAKE, FAKE, NULL) == 2
+    assert lib.losa_block_mass_noalloc(None, FAKE, FAKE, FAKE, NULL) == 1
+    assert lib.losa_block_mass_noalloc(desc(), FAKE, NULL, FAKE, NULL) == 1
+    assert lib.losa_block_mass_noalloc(desc(), FAKE, FAKE, NULL, NULL) == 1
