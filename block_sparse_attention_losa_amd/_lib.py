@@ -8,7 +8,10 @@ import ctypes
 import os
 import threading
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblosa.so")
+# LOSA_LIBRARY names another build of the same library (the host-sanitizer
+# test build); by default the in-tree liblosa.so is loaded
+LIB_PATH = os.environ.get("LOSA_LIBRARY") or \
+    os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblosa.so")
 
 LOSA_OK = 0
 STATUS_NAMES = {
@@ -68,6 +71,7 @@ SIGNATURES = {
     "losa_block_mass": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP, _VP, _VP]),
     "losa_block_mass_noalloc": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP]),
     "losa_dense_attn_mass_workspace": (ctypes.c_int64, [_DESC]),
+    "losa_dense_attn_mass_workspace_min": (ctypes.c_int64, [_DESC]),
     "losa_dense_attn_mass": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                             ctypes.c_int64, _VP]),
     "losa_select": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_double,
@@ -79,8 +83,8 @@ SIGNATURES = {
     "losa_sparse_attn": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "losa_sparse_plan_size": (ctypes.c_int64, [_DESC]),
     "losa_sparse_plan": (ctypes.c_int, [_DESC, _VP, _VP, ctypes.c_int64, _VP]),
-    "losa_sparse_attn_planned": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                                                _VP]),
+    "losa_sparse_attn_planned": (ctypes.c_int, [_DESC, _VP, _VP, _VP, _VP, _VP, _VP,
+                                                ctypes.c_int64, _VP, _VP, _VP]),
     "losa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "losa_version": (ctypes.c_int32, []),
 }

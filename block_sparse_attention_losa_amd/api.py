@@ -144,20 +144,27 @@ def block_mass_noalloc(q, k, block: int = 64, scale=None, mass=None):
     return mass
 
 
-def dense_attn_mass_workspace_bytes(q, block: int = 64) -> int:
-    """Workspace bytes :func:`dense_attn_mass` needs for inputs shaped like q."""
-    n = _lib.load().losa_dense_attn_mass_workspace(make_desc(q, block))
+def dense_attn_mass_workspace_bytes(q, block: int = 64, minimum: bool = False) -> int:
+    """Workspace bytes :func:`dense_attn_mass` needs for inputs shaped like q
+    to run every (b, h) in one pass, or with ``minimum`` the least it takes
+    (one (b, h) per pass)."""
+    lib = _lib.load()
+    fn = lib.losa_dense_attn_mass_workspace_min if minimum else lib.losa_dense_attn_mass_workspace
+    n = fn(make_desc(q, block))
     if n < 0:
         raise ValueError("unsupported shape for dense_attn_mass")
     return int(n)
 
 
 def dense_attn_mass(q, k, v, block: int = 64, scale=None, o=None, lse=None, mass=None,
-                    workspace=None, want_lse=True):
+                    workspace=None, want_lse=True, max_workspace_bytes=None):
     """Construction step in one sweep: dense attention and the block mass map
     of the same inputs.  Returns ``(o, lse, mass)``.  ``workspace`` is a
-    uint8 device tensor of at least :func:`dense_attn_mass_workspace_bytes`
-    bytes (allocated here when None)."""
+    uint8 device tensor of at least ``dense_attn_mass_workspace_bytes(q,
+    block, minimum=True)`` bytes; the call makes as few passes over the
+    heads as its size allows.  When None, one is allocated here: the full
+    size, or at most ``max_workspace_bytes`` (but never below the minimum).
+    The results do not depend on the workspace size."""
     _check_inputs(lse, mass, workspace, strided=(q, k, v, o))
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share shape and dtype")
@@ -176,8 +183,11 @@ def dense_attn_mass(q, k, v, block: int = 64, scale=None, o=None, lse=None, mass
     if mass is None:
         mass = torch.empty((b, h, nb, nb), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = torch.empty(dense_attn_mass_workspace_bytes(q, block), dtype=torch.uint8,
-                                device=q.device)
+        size = dense_attn_mass_workspace_bytes(q, block)
+        if max_workspace_bytes is not None:
+            size = max(min(size, int(max_workspace_bytes)),
+                       dense_attn_mass_workspace_bytes(q, block, minimum=True))
+        workspace = torch.empty(size, dtype=torch.uint8, device=q.device)
     lib = _lib.load()
     _lib.check("losa_dense_attn_mass", lib.losa_dense_attn_mass(
         desc, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(mass), _ptr(workspace),
@@ -316,14 +326,14 @@ def sparse_attn(q, k, v, idx, count, block: int = 64, scale=None, o=None, lse=No
         lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
     lib = _lib.load()
     if plan is not None:
-        if plan.dtype != torch.int32:
-            raise TypeError("plan must be int32")
+        if plan.dtype != torch.int32 or not plan.is_contiguous():
+            raise TypeError("plan must be a contiguous int32 tensor")
         # the kernel reads one plan entry per launched workgroup
         if plan.numel() * 4 < lib.losa_sparse_plan_size(desc):
             raise ValueError("plan is smaller than sparse_plan makes for these shapes")
         _lib.check("losa_sparse_attn_planned", lib.losa_sparse_attn_planned(
-            desc, _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(count), _ptr(plan), _ptr(o),
-            _ptr(lse), _stream(q)))
+            desc, _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(count), _ptr(plan),
+            plan.numel() * 4, _ptr(o), _ptr(lse), _stream(q)))
         return o, lse
     _lib.check("losa_sparse_attn", lib.losa_sparse_attn(
         desc, _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(count), _ptr(o), _ptr(lse),

@@ -2,6 +2,14 @@
 
 Usage: ``python -m block_sparse_attention_losa_amd.build`` (or call
 :func:`build`).  Every call recompiles.
+
+``python -m block_sparse_attention_losa_amd.build --host-sanitizers``
+builds instead a CPU-side test library, ``_build/asan/liblosa_asan.so``:
+the host code of every source with AddressSanitizer and
+UndefinedBehaviorSanitizer (the device code is built as usual, without
+them).  It is loaded through ``LOSA_LIBRARY`` with the sanitizer runtime
+preloaded (:func:`sanitizer_runtime`), to run the C-ABI's host-side checks
+under the sanitizers on a machine without a GPU; it is never used on one.
 """
 
 import concurrent.futures
@@ -49,6 +57,56 @@ def _compile(src: str) -> str:
     return obj
 
 
+ASAN_DIR = os.path.join(OBJ_DIR, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "liblosa_asan.so")
+# host code only; each sanitizer flag is scoped to the host compilation
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def _compile_sanitized(src: str) -> str:
+    obj = os.path.join(ASAN_DIR, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + COMMON + SANITIZE
+    if src.endswith(".hip"):
+        cmd += ["-x", "hip", f"--offload-arch={ARCH}"] + DEVICE_FLAGS
+    else:
+        cmd += ["-D__HIP_PLATFORM_AMD__"]
+    cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    return obj
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The CPU-side test library with host sanitizers (see the module doc)."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+        objs = list(ex.map(_compile_sanitized, HIP_SOURCES + HOST_SOURCES))
+    tmp = ASAN_LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Xarch_host",
+           "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan",
+           "-o", tmp] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, ASAN_LIB)
+    if verbose:
+        print(f"built {ASAN_LIB}")
+    return ASAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (to preload)."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the AddressSanitizer runtime of the compiler was not found")
+    return path
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
@@ -65,5 +123,8 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--host-sanitizers" in sys.argv[1:]:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -94,8 +94,18 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   // a plan (sparse only) gives the item of each workgroup directly: items
   // ranked by descending cost and dealt to the XCDs in runs of neighbouring
   // query blocks, so every XCD gets the same mix and starts with its longest
-  // items (layout in frozen_lists.hip); -1 marks an unused slot
-  const int item = p.order != nullptr ? p.order[blockIdx.x] : xcd_item(blockIdx.x, wph, bh_count);
+  // items (layout in frozen_lists.hip); -1 marks an unused slot.  A plan
+  // whose header names another shape is not followed: the workgroups then
+  // take the items in index order (the grid has a slot for each), so every
+  // row is still written
+  int item;
+  if (p.order != nullptr) {
+    const bool match = p.order[0] == kPlanMagic && p.order[1] == wph * bh_count &&
+                       p.order[2] == nb && p.order[3] == G::kQPW;
+    item = match ? p.order[kPlanHeader + blockIdx.x] : (int)blockIdx.x;
+  } else {
+    item = xcd_item(blockIdx.x, wph, bh_count);
+  }
   // padding of the XCD-aware grid; a plan entry outside the items is ignored
   if (item < 0 || item >= wph * bh_count) return;
   const int bh = item / wph;

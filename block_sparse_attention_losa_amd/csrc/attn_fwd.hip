@@ -1,4 +1,5 @@
-// Flash-style attention passes of the LoSA hot path on gfx950 (CDNA4):
+// fp32 attention passes of the LoSA hot path on gfx950 (CDNA4), for fp32
+// inputs (the bf16 passes are in attn_bf16.hip):
 //   kDense  - softmax attention over every key block (dense baseline and the
 //             construction step's first pass), writes O and lse;
 //   kSparse - the same over the frozen key-block list of each query block;
@@ -13,23 +14,19 @@
 // row group split every 64-key tile in halves and merge their partial
 // softmax states at the end.
 //
-// Scores are computed transposed, S^T = K Q^T, on 32x32 MFMA tiles: a lane
-// then holds one query row and 16 of the 32 keys, so row maxima and sums
-// need one cross-half exchange only, and the probabilities already sit in
-// the B-operand layout of O^T += V^T P^T.  The K rows fed to the A operand
-// are permuted (bits 2 and 3 of the row swapped) so that each lane's eight
-// bf16 probabilities of a 16-key slice are consecutive keys, which lets V^T
-// be read with one 16-byte LDS load per MFMA.
-#include <type_traits>
+// Scores are computed transposed, S^T = K Q^T, on 32x32x2 fp32 MFMA tiles:
+// a lane then holds one query row and 16 of the 32 keys, so row maxima and
+// sums need one cross-half exchange only, and the probabilities already sit
+// in the B-operand layout of O^T += V^T P^T.  This path exists for exact
+// fp32 inputs (the tiny reference case), not for speed.
 
 #include "losa_device.h"
 #include "losa_launch.h"
 
 namespace losa {
 
-template <typename T, int D, int BQ, int MODE>
+template <int D, int BQ, int MODE>
 struct Geo {
-  static constexpr bool kBf16 = std::is_same<T, bf16>::value;
   static constexpr bool kWithV = (MODE == kDense || MODE == kSparse);
   static constexpr int kThreads = 256;
   static constexpr int kRG = BQ / 32;          // row groups of 32 rows
@@ -37,10 +34,10 @@ struct Geo {
   static constexpr int kKT = 64;               // keys per staged tile
   static constexpr int kCPW = 2 / kKS;         // 32-key chunks per wave per tile
   static constexpr int kSubs = BQ / 64;        // staged tiles per key block
-  static constexpr int kKStr = kBf16 ? D + 8 : D + 4;   // K row stride (elements)
-  static constexpr int kVStr = kBf16 ? 72 : D + 4;      // bf16: V^T row; fp32: V row
-  static constexpr int kKBytes = kKT * kKStr * (int)sizeof(T);
-  static constexpr int kVBytes = !kWithV ? 0 : (kBf16 ? D * kVStr * 2 : kKT * kVStr * 4);
+  static constexpr int kKStr = D + 4;                   // K row stride (elements)
+  static constexpr int kVStr = D + 4;                   // V row stride (elements)
+  static constexpr int kKBytes = kKT * kKStr * 4;
+  static constexpr int kVBytes = kWithV ? kKT * kVStr * 4 : 0;
   static constexpr int kStage = kKBytes + kVBytes;
   static constexpr int kStages = 2 * kStage;
   static constexpr int kMaxBlocks = 1024;
@@ -49,27 +46,9 @@ struct Geo {
   static constexpr int kCombineBytes = (kKS == 2) ? kRG * (2 + (kWithV ? D : 0)) * 32 * 4 : 0;
   static_assert(kCombineBytes <= kStages, "combine buffer must fit in the stage buffers");
   static constexpr int kLdsBytes = kStages + kAuxBytes;
-  // K chunks of 16 bytes per thread per tile
-  static constexpr int kKChunks = kKT * D * (int)sizeof(T) / 16 / kThreads;
-  // fp32 V chunks of 16 bytes per thread (row-major copy)
-  static constexpr int kVChunksF = kBf16 ? 0 : kKChunks;
+  // K (and V) chunks of 16 bytes per thread per tile
+  static constexpr int kKChunks = kKT * D * 4 / 16 / kThreads;
 };
-
-// Key offset (within a 32-key chunk) of the S^T row fed by A-operand row r.
-template <bool BF16>
-__device__ __forceinline__ int key_of_row(int r) {
-  if constexpr (BF16) {
-    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-  } else {
-    return r;
-  }
-}
-
-// Key offset (within a 32-key chunk) held by score register i of half g.
-template <bool BF16>
-__device__ __forceinline__ int key_of_reg(int i, int g) {
-  return key_of_row<BF16>(c_row(i, g));
-}
 
 // ---------------------------------------------------------------------------
 // Frozen list -> ascending block order in LDS.  Visiting kept blocks in
@@ -108,16 +87,10 @@ __device__ int build_ascending_list(const int32_t* __restrict__ idx_row, int cnt
 }
 
 // ---------------------------------------------------------------------------
-// fp32 at D = 128 needs more than 256 registers per lane: one wave per SIMD.
-template <typename T, int D>
-constexpr int waves_per_simd() {
-  return (std::is_same<T, float>::value && D == 128) ? 1 : 2;
-}
-
-template <typename T, int D, int BQ, int MODE>
-__global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(AttnParams p) {
-  using G = Geo<T, D, BQ, MODE>;
-  constexpr bool BF = G::kBf16;
+// D = 128 needs more than 256 registers per lane: one wave per SIMD.
+template <int D, int BQ, int MODE>
+__global__ void __launch_bounds__(256, (D == 128 ? 1 : 2)) attn_kernel(AttnParams p) {
+  using G = Geo<D, BQ, MODE>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int item = xcd_item(blockIdx.x, p.nb, p.items / p.nb);
@@ -126,9 +99,9 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
   const int bh = item / nb;
   const int qb = item - bh * nb;
   const size_t head_off = (size_t)bh * (size_t)N * D;
-  const T* __restrict__ qh = (const T*)p.q + head_off;
-  const T* __restrict__ kh = (const T*)p.k + head_off;
-  const T* __restrict__ vh = (const T*)p.v + head_off;
+  const float* __restrict__ qh = (const float*)p.q + head_off;
+  const float* __restrict__ kh = (const float*)p.k + head_off;
+  const float* __restrict__ vh = (const float*)p.v + head_off;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
@@ -165,37 +138,26 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
   if (G::kSubs == 2 && nblk > 0 && block_at(nblk - 1) == nb - 1 && (nb - 1) * BQ + 64 >= N)
     --nstage;  // empty second half of a short last block
 
-  // ---- Q^T as the B operand, kept in registers
-  constexpr int kQRegs = BF ? D / 16 : D / 2;
-  using QElem = typename std::conditional<BF, bf16x8, float>::type;
-  QElem qreg[kQRegs];
-  constexpr int kRowBytes = D * (int)sizeof(T);
+  // ---- Q^T as the B operand, kept in registers: lane half g holds head
+  // dims g*D/2 .. g*D/2 + D/2 - 1 of its row
+  float qreg[D / 2];
+  constexpr int kRowBytes = D * 4;
   {
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(qh, N * kRowBytes);
-    if constexpr (BF) {
 #pragma unroll
-      for (int dk = 0; dk < D / 16; ++dk)
-        qreg[dk] = __builtin_bit_cast(bf16x8, buf_load16(qr, row * kRowBytes + dk * 32 + g * 16));
-    } else {
-#pragma unroll
-      for (int s = 0; s < D / 2; s += 4) {
-        const u32x4 x = buf_load16(qr, row * kRowBytes + (g * (D / 2) + s) * 4);
-        qreg[s] = __uint_as_float(x[0]);
-        qreg[s + 1] = __uint_as_float(x[1]);
-        qreg[s + 2] = __uint_as_float(x[2]);
-        qreg[s + 3] = __uint_as_float(x[3]);
-      }
+    for (int s = 0; s < D / 2; s += 4) {
+      const u32x4 x = buf_load16(qr, row * kRowBytes + (g * (D / 2) + s) * 4);
+      qreg[s] = __uint_as_float(x[0]);
+      qreg[s + 1] = __uint_as_float(x[1]);
+      qreg[s + 2] = __uint_as_float(x[2]);
+      qreg[s + 3] = __uint_as_float(x[3]);
     }
   }
 
-  // ---- stage registers (global -> regs -> LDS)
-  u32x4 kr[G::kKChunks];
-  u32x4 vr[BF ? 4 : G::kVChunksF];
-  const bool v_thread = BF ? (tid < 2 * D) : true;  // bf16 V^T: 2*D blocks of 4 keys x 8 dims
-
-  // per-lane byte offsets inside a tile; the tile itself is addressed by a
+  // ---- stage registers (global -> regs -> LDS); the tile is addressed by a
   // scalar buffer resource starting at its first key
-  const int v_kgrp = tid & 15, v_dgrp = tid >> 4;
+  u32x4 kr[G::kKChunks];
+  u32x4 vr[G::kKChunks];
   auto load_k = [&](int key0) {
     const int bytes = (N - key0) * kRowBytes;
     const __amdgpu_buffer_rsrc_t kt =
@@ -208,60 +170,32 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
       const int bytes = (N - key0) * kRowBytes;
       const __amdgpu_buffer_rsrc_t vt =
           make_rsrc((const unsigned char*)vh + (size_t)key0 * kRowBytes, bytes);
-      if constexpr (BF) {
-        if (v_thread) {
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            vr[jj] = buf_load16(vt, (v_kgrp * 4 + jj) * kRowBytes + v_dgrp * 16);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < G::kVChunksF; ++j) vr[j] = buf_load16(vt, (j * 256 + tid) * 16);
-      }
+      for (int j = 0; j < G::kKChunks; ++j) vr[j] = buf_load16(vt, (j * 256 + tid) * 16);
     }
   };
 
-  // LDS: two K tiles, then two V tiles (bf16: V^T)
-  auto kbuf = [&](int b) -> T* { return (T*)(smem + b * G::kKBytes); };
-  auto vbuf = [&](int b) -> T* { return (T*)(smem + 2 * G::kKBytes + b * G::kVBytes); };
+  // LDS: two K tiles, then two V tiles, both row-major with padded rows
+  auto kbuf = [&](int b) -> float* { return (float*)(smem + b * G::kKBytes); };
+  auto vbuf = [&](int b) -> float* { return (float*)(smem + 2 * G::kKBytes + b * G::kVBytes); };
 
   auto store_k = [&](int b) {
-    T* klds = kbuf(b);
+    float* klds = kbuf(b);
 #pragma unroll
     for (int j = 0; j < G::kKChunks; ++j) {
       const int c = j * 256 + tid;
-      const int key = c / (D * (int)sizeof(T) / 16);
-      const int col = c % (D * (int)sizeof(T) / 16);
-      *(u32x4*)((unsigned char*)(klds + key * G::kKStr) + col * 16) = kr[j];
+      const int key = c / (D / 4), col = c % (D / 4);
+      *(u32x4*)(klds + key * G::kKStr + col * 4) = kr[j];
     }
   };
   auto store_v = [&](int b) {
     if constexpr (G::kWithV) {
-      T* vlds = vbuf(b);
-      if constexpr (BF) {
-        if (v_thread) {
+      float* vlds = vbuf(b);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int w = i >> 1;
-            unsigned x, y;
-            if ((i & 1) == 0) {
-              x = (vr[0][w] & 0xFFFFu) | (vr[1][w] << 16);
-              y = (vr[2][w] & 0xFFFFu) | (vr[3][w] << 16);
-            } else {
-              x = (vr[0][w] >> 16) | (vr[1][w] & 0xFFFF0000u);
-              y = (vr[2][w] >> 16) | (vr[3][w] & 0xFFFF0000u);
-            }
-            u32x2 xy = {x, y};
-            *(u32x2*)(vlds + (v_dgrp * 8 + i) * G::kVStr + v_kgrp * 4) = xy;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < G::kVChunksF; ++j) {
-          const int c = j * 256 + tid;
-          const int key = c / (D / 4), col = c % (D / 4);
-          *(u32x4*)(vlds + key * G::kVStr + col * 4) = vr[j];
-        }
+      for (int j = 0; j < G::kKChunks; ++j) {
+        const int c = j * 256 + tid;
+        const int key = c / (D / 4), col = c % (D / 4);
+        *(u32x4*)(vlds + key * G::kVStr + col * 4) = vr[j];
       }
     }
   };
@@ -286,28 +220,20 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
 
   // S^T of this wave's chunks of the K tile in buffer b
   auto compute_s = [&](int b, f32x16 (&sc)[G::kCPW]) {
-    const T* klds = kbuf(b);
+    const float* klds = kbuf(b);
 #pragma unroll
     for (int cc = 0; cc < G::kCPW; ++cc) {
       const int chunk = G::kKS == 2 ? ks : cc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[cc][i] = 0.f;
-      const T* krow = klds + (chunk * 32 + key_of_row<BF>(l32)) * G::kKStr;
-      if constexpr (BF) {
+      const float* krow = klds + (chunk * 32 + l32) * G::kKStr;
 #pragma unroll
-        for (int dk = 0; dk < D / 16; ++dk) {
-          const bf16x8 a = *(const bf16x8*)(krow + dk * 16 + g * 8);
-          sc[cc] = mfma_bf16(a, qreg[dk], sc[cc]);
-        }
-      } else {
-#pragma unroll
-        for (int st = 0; st < D / 2; st += 4) {
-          const float4 a = *(const float4*)(krow + g * (D / 2) + st);
-          sc[cc] = mfma_f32(a.x, qreg[st], sc[cc]);
-          sc[cc] = mfma_f32(a.y, qreg[st + 1], sc[cc]);
-          sc[cc] = mfma_f32(a.z, qreg[st + 2], sc[cc]);
-          sc[cc] = mfma_f32(a.w, qreg[st + 3], sc[cc]);
-        }
+      for (int st = 0; st < D / 2; st += 4) {
+        const float4 a = *(const float4*)(krow + g * (D / 2) + st);
+        sc[cc] = mfma_f32(a.x, qreg[st], sc[cc]);
+        sc[cc] = mfma_f32(a.y, qreg[st + 1], sc[cc]);
+        sc[cc] = mfma_f32(a.z, qreg[st + 2], sc[cc]);
+        sc[cc] = mfma_f32(a.w, qreg[st + 3], sc[cc]);
       }
     }
   };
@@ -324,7 +250,7 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
         const int chunk = G::kKS == 2 ? ks : cc;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (key0 + chunk * 32 + key_of_reg<BF>(i, g) >= N) sc[cc][i] = -INFINITY;
+          if (key0 + chunk * 32 + c_row(i, g) >= N) sc[cc][i] = -INFINITY;
       }
     }
     if constexpr (MODE == kMass) {
@@ -370,36 +296,17 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[mt][i] *= alpha;
         }
-        const T* vlds = vbuf(t & 1);
+        const float* vlds = vbuf(t & 1);
 #pragma unroll
         for (int cc = 0; cc < G::kCPW; ++cc) {
           const int chunk = G::kKS == 2 ? ks : cc;
-          if constexpr (BF) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              u32x4 pk;
-              pk[0] = pack_bf16x2(pr[cc][8 * h + 0], pr[cc][8 * h + 1]);
-              pk[1] = pack_bf16x2(pr[cc][8 * h + 2], pr[cc][8 * h + 3]);
-              pk[2] = pack_bf16x2(pr[cc][8 * h + 4], pr[cc][8 * h + 5]);
-              pk[3] = pack_bf16x2(pr[cc][8 * h + 6], pr[cc][8 * h + 7]);
-              const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
+          for (int mt = 0; mt < kORegs; ++mt)
 #pragma unroll
-              for (int mt = 0; mt < kORegs; ++mt) {
-                const bf16x8 a = *(const bf16x8*)(vlds + (mt * 32 + l32) * G::kVStr +
-                                                  chunk * 32 + h * 16 + g * 8);
-                oacc[mt] = mfma_bf16(a, pb, oacc[mt]);
-              }
+            for (int i = 0; i < 16; ++i) {
+              const float a = vlds[(chunk * 32 + c_row(i, g)) * G::kVStr + mt * 32 + l32];
+              oacc[mt] = mfma_f32(a, pr[cc][i], oacc[mt]);
             }
-          } else {
-#pragma unroll
-            for (int mt = 0; mt < kORegs; ++mt)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                const float a =
-                    vlds[(chunk * 32 + key_of_reg<BF>(i, g)) * G::kVStr + mt * 32 + l32];
-                oacc[mt] = mfma_f32(a, pr[cc][i], oacc[mt]);
-              }
-          }
         }
       }
     }
@@ -486,7 +393,7 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
     }
     if constexpr (G::kWithV) {
       const float inv = empty ? 0.f : 1.0f / l_tot;
-      T* orow = (T*)p.o + head_off + (size_t)row * D;
+      float* orow = (float*)p.o + head_off + (size_t)row * D;
 #pragma unroll
       for (int mt = 0; mt < kORegs; ++mt)
 #pragma unroll
@@ -494,22 +401,17 @@ __global__ void __launch_bounds__(256, (waves_per_simd<T, D>())) attn_kernel(Att
           const int d0 = mt * 32 + 8 * i4 + 4 * g;
           const float x0 = oacc[mt][4 * i4 + 0] * inv, x1 = oacc[mt][4 * i4 + 1] * inv;
           const float x2 = oacc[mt][4 * i4 + 2] * inv, x3 = oacc[mt][4 * i4 + 3] * inv;
-          if constexpr (BF) {
-            u32x2 w = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
-            *(u32x2*)(orow + d0) = w;
-          } else {
-            *(float4*)(orow + d0) = make_float4(x0, x1, x2, x3);
-          }
+          *(float4*)(orow + d0) = make_float4(x0, x1, x2, x3);
         }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int D, int BQ, int MODE>
+template <int D, int BQ, int MODE>
 static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
-  using G = Geo<T, D, BQ, MODE>;
-  auto kern = attn_kernel<T, D, BQ, MODE>;
+  using G = Geo<D, BQ, MODE>;
+  auto kern = attn_kernel<D, BQ, MODE>;
   static std::atomic<bool> lds_set[kMaxDevices];
   const hipError_t attr = set_lds_limit(kern, G::kLdsBytes, lds_set);
   if (attr != hipSuccess) return attr;
@@ -517,31 +419,30 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D, int BQ>
+template <int D, int BQ>
 static hipError_t launch_mode(int mode, const AttnParams& p, hipStream_t stream) {
   switch (mode) {
-    case kDense: return launch_one<T, D, BQ, kDense>(p, stream);
-    case kSparse: return launch_one<T, D, BQ, kSparse>(p, stream);
-    case kLse: return launch_one<T, D, BQ, kLse>(p, stream);
-    case kMass: return launch_one<T, D, BQ, kMass>(p, stream);
+    case kDense: return launch_one<D, BQ, kDense>(p, stream);
+    case kSparse: return launch_one<D, BQ, kSparse>(p, stream);
+    case kLse: return launch_one<D, BQ, kLse>(p, stream);
+    case kMass: return launch_one<D, BQ, kMass>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T>
-static hipError_t launch_dtype(int mode, int head_dim, int block, const AttnParams& p,
-                               hipStream_t stream) {
-  if (head_dim == 64 && block == 64) return launch_mode<T, 64, 64>(mode, p, stream);
-  if (head_dim == 64 && block == 128) return launch_mode<T, 64, 128>(mode, p, stream);
-  if (head_dim == 128 && block == 64) return launch_mode<T, 128, 64>(mode, p, stream);
-  if (head_dim == 128 && block == 128) return launch_mode<T, 128, 128>(mode, p, stream);
+static hipError_t launch_fp32(int mode, int head_dim, int block, const AttnParams& p,
+                              hipStream_t stream) {
+  if (head_dim == 64 && block == 64) return launch_mode<64, 64>(mode, p, stream);
+  if (head_dim == 64 && block == 128) return launch_mode<64, 128>(mode, p, stream);
+  if (head_dim == 128 && block == 64) return launch_mode<128, 64>(mode, p, stream);
+  if (head_dim == 128 && block == 128) return launch_mode<128, 128>(mode, p, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn(int mode, int dtype, int head_dim, int block, const AttnParams& p,
                        hipStream_t stream) {
   if (dtype == 0) return launch_attn_bf16(mode, head_dim, block, p, stream);
-  if (dtype == 1) return launch_dtype<float>(mode, head_dim, block, p, stream);
+  if (dtype == 1) return launch_fp32(mode, head_dim, block, p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -73,7 +73,8 @@ __global__ void __launch_bounds__(256) retained_mass_kernel(const float* __restr
   if (lane == 0) retained[item] = acc / (float)rows;
 }
 
-// Plan layout.  Items are ranked by cost, descending, in kPlanBuckets
+// Plan layout (after the header that names the shape, losa_launch.h).
+// Items are ranked by cost, descending, in kPlanBuckets
 // buckets (cost * kPlanBuckets / (nb + 1)); within a bucket they keep their
 // index order (head-major, query blocks ascending), so runs of consecutive
 // ranks are neighbouring query blocks of one head, whose lists overlap.
@@ -117,6 +118,13 @@ __global__ void __launch_bounds__(1024) sparse_plan_kernel(const int32_t* __rest
       c = max(c, min(max(count[(size_t)bh * nb + q], 0), nb));
     return min(kPlanBuckets - 1, c * kPlanBuckets / (nb + 1));
   };
+  if (tid == 0) {
+    order[0] = kPlanMagic;
+    order[1] = n_items;
+    order[2] = nb;
+    order[3] = qpw;
+  }
+  order += kPlanHeader;
   if (tid < kPlanBuckets) start[tid] = 0;
   __syncthreads();
   for (int item = tid; item < n_items; item += 1024) atomicAdd(&start[bucket_of(item)], 1);

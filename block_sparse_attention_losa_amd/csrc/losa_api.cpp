@@ -2,8 +2,10 @@
 // kernels.  Every check happens before anything is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 
 #include "../../include/losa.h"
 #include "losa_launch.h"
@@ -107,16 +109,17 @@ losa::AttnParams base_params(const losa_attn_desc* d, int32_t nb) {
 
 losa_status device_status(hipError_t e) { return e == hipSuccess ? LOSA_OK : LOSA_ERR_DEVICE; }
 
-// Workspace of losa_dense_attn_mass: the per-row block sums [B*H, nb, N]
-// fp32, then the per-row offsets [B*H, N] fp32 at the next 256-byte
-// boundary.
-int64_t rowsum_bytes(const losa_attn_desc* d, int32_t nb) {
-  const int64_t raw = int64_t{4} * d->batch * d->heads * nb * d->seq_len;
+// Workspace of losa_dense_attn_mass for a pass over `heads` (b, h) slices:
+// the per-row block sums [heads, nb, N] fp32, then the per-row offsets
+// [heads, N] fp32 at the next 256-byte boundary.
+int64_t rowsum_bytes(const losa_attn_desc* d, int32_t nb, int64_t heads) {
+  const int64_t raw = int64_t{4} * heads * nb * d->seq_len;
   return (raw + 255) / 256 * 256;
 }
-int64_t dense_mass_workspace(const losa_attn_desc* d, int32_t nb) {
-  return rowsum_bytes(d, nb) + int64_t{4} * d->batch * d->heads * d->seq_len;
+int64_t dense_mass_workspace(const losa_attn_desc* d, int32_t nb, int64_t heads) {
+  return rowsum_bytes(d, nb, heads) + int64_t{4} * heads * d->seq_len;
 }
+int64_t all_heads(const losa_attn_desc* d) { return int64_t{d->batch} * d->heads; }
 
 // Sparse work items: one per workgroup of the sparse kernel, i.e. per
 // losa::attn_rows query rows of each (b, h).
@@ -128,7 +131,7 @@ int64_t plan_items(const losa_attn_desc* d, int32_t nb) {
   return int64_t{d->batch} * d->heads * ((nb + qpw - 1) / qpw);
 }
 int64_t plan_entries(const losa_attn_desc* d, int32_t nb) {
-  return losa::sparse_plan_slots(plan_items(d, nb));
+  return losa::kPlanHeader + losa::sparse_plan_slots(plan_items(d, nb));
 }
 
 }  // namespace
@@ -190,7 +193,13 @@ losa_status losa_block_mass(const losa_attn_desc* desc, const void* q, const voi
 int64_t losa_dense_attn_mass_workspace(const losa_attn_desc* desc) {
   int32_t nb = 0;
   if (check_desc(desc, &nb) != LOSA_OK) return -1;
-  return dense_mass_workspace(desc, nb);
+  return dense_mass_workspace(desc, nb, all_heads(desc));
+}
+
+int64_t losa_dense_attn_mass_workspace_min(const losa_attn_desc* desc) {
+  int32_t nb = 0;
+  if (check_desc(desc, &nb) != LOSA_OK) return -1;
+  return dense_mass_workspace(desc, nb, 1);
 }
 
 losa_status losa_dense_attn_mass(const losa_attn_desc* desc, const void* q, const void* k,
@@ -203,39 +212,75 @@ losa_status losa_dense_attn_mass(const losa_attn_desc* desc, const void* q, cons
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(mass, 4) || !aligned(workspace, 256) || (lse && !aligned(lse, 4)))
     return LOSA_ERR_MISALIGNED;
-  if (workspace_bytes < dense_mass_workspace(desc, nb)) return LOSA_ERR_WORKSPACE;
+  if (workspace_bytes < dense_mass_workspace(desc, nb, 1)) return LOSA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* rowsum = static_cast<float*>(workspace);
-  float* rowref = reinterpret_cast<float*>(static_cast<char*>(workspace) + rowsum_bytes(desc, nb));
-  losa::AttnParams p = base_params(desc, nb);
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = o;
-  if (desc->dtype == LOSA_FP32) {
-    // fp32: the dense pass writes lse (into the workspace when the caller
-    // wants none) and the two-pass mass kernel reads it
-    float* lse_buf = lse ? lse : rowref;
-    p.lse = lse_buf;
-    st = device_status(losa::launch_attn(losa::kDense, desc->dtype, desc->head_dim, desc->block,
-                                         p, s));
-    if (st != LOSA_OK) return st;
-    p.o = nullptr;
-    p.v = nullptr;
-    p.lse = nullptr;
-    p.lse_in = lse_buf;
-    p.mass = mass;
-    return device_status(
-        losa::launch_attn(losa::kMass, desc->dtype, desc->head_dim, desc->block, p, s));
+  const losa::AttnParams base = base_params(desc, nb);
+  // Heads per pass: every (b, h) at once when the whole workspace is given;
+  // otherwise passes over runs of the heads of one batch item, as many as
+  // the workspace holds (the per-row arithmetic is the same either way, so
+  // are the results)
+  int64_t group = all_heads(desc);
+  if (workspace_bytes < dense_mass_workspace(desc, nb, group)) {
+    group = desc->heads;
+    while (group > 1 && dense_mass_workspace(desc, nb, group) > workspace_bytes) --group;
   }
-  p.lse = lse;
-  p.rowsum = rowsum;
-  p.rowref = rowref;
-  st = device_status(
-      losa::launch_attn(losa::kDenseMass, desc->dtype, desc->head_dim, desc->block, p, s));
-  if (st != LOSA_OK) return st;
-  return device_status(losa::launch_mass_fold(rowsum, rowref, mass, desc->seq_len, nb,
-                                              desc->block, desc->batch * desc->heads, s));
+  const int64_t esize = desc->dtype == LOSA_FP32 ? 4 : 2;
+  const int64_t nn = desc->seq_len;
+  const int64_t passes_per_batch = group >= all_heads(desc) ? 1 : (desc->heads + group - 1) / group;
+  const int32_t batches = group >= all_heads(desc) ? 1 : desc->batch;
+  for (int32_t b = 0; b < batches; ++b) {
+    for (int64_t pass = 0; pass < passes_per_batch; ++pass) {
+      const int64_t h0 = pass * group;
+      const int64_t g = group >= all_heads(desc) ? group : std::min<int64_t>(group, desc->heads - h0);
+      const int64_t first = int64_t{b} * desc->heads + h0;  // first (b, h) of the pass
+      losa::AttnParams p = base;
+      if (g < all_heads(desc)) {
+        // the pass sees its g heads of batch item b as heads 0..g-1 of one
+        // batch item: base pointers moved to head (b, h0), head strides kept
+        p.heads = static_cast<int32_t>(g);
+        p.items = static_cast<int32_t>(g * nb);
+      }
+      const int64_t in_off = (b * base.stride_b + h0 * base.stride_h) * esize;
+      const int64_t out_off = (b * base.o_stride_b + h0 * base.o_stride_h) * esize;
+      p.q = static_cast<const char*>(q) + in_off;
+      p.k = static_cast<const char*>(k) + in_off;
+      p.v = static_cast<const char*>(v) + in_off;
+      p.o = static_cast<char*>(o) + out_off;
+      float* lse_g = lse ? lse + first * nn : nullptr;
+      float* mass_g = mass + first * nb * nb;
+      float* rowsum = static_cast<float*>(workspace);
+      float* rowref =
+          reinterpret_cast<float*>(static_cast<char*>(workspace) + rowsum_bytes(desc, nb, g));
+      if (desc->dtype == LOSA_FP32) {
+        // fp32: the dense pass writes lse (into the workspace when the caller
+        // wants none) and the two-pass mass kernel reads it
+        float* lse_buf = lse_g ? lse_g : rowref;
+        p.lse = lse_buf;
+        st = device_status(losa::launch_attn(losa::kDense, desc->dtype, desc->head_dim,
+                                             desc->block, p, s));
+        if (st != LOSA_OK) return st;
+        p.o = nullptr;
+        p.v = nullptr;
+        p.lse = nullptr;
+        p.lse_in = lse_buf;
+        p.mass = mass_g;
+        st = device_status(
+            losa::launch_attn(losa::kMass, desc->dtype, desc->head_dim, desc->block, p, s));
+        if (st != LOSA_OK) return st;
+        continue;
+      }
+      p.lse = lse_g;
+      p.rowsum = rowsum;
+      p.rowref = rowref;
+      st = device_status(losa::launch_attn(losa::kDenseMass, desc->dtype, desc->head_dim,
+                                           desc->block, p, s));
+      if (st != LOSA_OK) return st;
+      st = device_status(losa::launch_mass_fold(rowsum, rowref, mass_g, desc->seq_len, nb,
+                                                desc->block, static_cast<int32_t>(g), s));
+      if (st != LOSA_OK) return st;
+    }
+  }
+  return LOSA_OK;
 }
 
 losa_status losa_select(int32_t rows, int32_t nkb, const float* mass, double threshold,
@@ -325,12 +370,14 @@ losa_status losa_sparse_plan(const losa_attn_desc* desc, const int32_t* count, i
 
 losa_status losa_sparse_attn_planned(const losa_attn_desc* desc, const void* q, const void* k,
                                      const void* v, const int32_t* idx, const int32_t* count,
-                                     const int32_t* plan, void* o, float* lse, void* stream) {
+                                     const int32_t* plan, int64_t plan_bytes, void* o,
+                                     float* lse, void* stream) {
   if (plan == nullptr) return LOSA_ERR_NULL_POINTER;
   if (!aligned(plan, 4)) return LOSA_ERR_MISALIGNED;
   int32_t nb = 0;
   losa_status st = check_desc(desc, &nb);
   if (st != LOSA_OK) return st;
+  if (plan_bytes < 4 * plan_entries(desc, nb)) return LOSA_ERR_WORKSPACE;
   if (!q || !k || !v || !o || !idx || !count) return LOSA_ERR_NULL_POINTER;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(idx, 4) || !aligned(count, 4) || (lse && !aligned(lse, 4)))
@@ -349,7 +396,12 @@ losa_status losa_sparse_attn_planned(const losa_attn_desc* desc, const void* q, 
 }
 
 const char* losa_status_string(losa_status status) {
-  switch (status) {
+  // A C caller may pass any int: read the argument's bits as an int rather
+  // than load an out-of-range value of the C++ enum type (undefined there)
+  int code = 0;
+  static_assert(sizeof(code) == sizeof(status), "losa_status is int-sized");
+  std::memcpy(&code, &status, sizeof(code));
+  switch (code) {
     case LOSA_OK: return "ok";
     case LOSA_ERR_NULL_POINTER: return "a required pointer is NULL";
     case LOSA_ERR_BAD_SHAPE: return "unsupported sizes (D, block, N, B*H*nb or nkb)";
@@ -367,6 +419,6 @@ const char* losa_status_string(losa_status status) {
   return "unknown status";
 }
 
-int32_t losa_version(void) { return 100; }
+int32_t losa_version(void) { return 200; }
 
 }  // extern "C"

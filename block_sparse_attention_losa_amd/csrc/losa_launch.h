@@ -94,7 +94,12 @@ hipError_t launch_select(int32_t rows, int32_t nkb, const float* mass, double ta
 // Dispatch order for the sparse kernel: the work items (bh * wph + w, one per
 // group of qpw query blocks) ranked by descending cost, cost = the largest
 // count among the group's query blocks, laid out per XCD (frozen_lists.hip).
-// order: [sparse_plan_slots(bh_count * wph)] int32, -1 in unused slots.
+// order: a header of kPlanHeader int32 words {kPlanMagic, n_items, nb, qpw}
+// naming the shape the plan was made for, then sparse_plan_slots(n_items)
+// slots (n_items = bh_count * wph), -1 in unused slots.  The sparse kernel
+// follows the slots only when the header matches its own shape.
+constexpr int kPlanHeader = 4;
+constexpr int32_t kPlanMagic = 0x4153'6F4C;  // "LoSA"
 long long sparse_plan_slots(long long n_items);
 hipError_t launch_sparse_plan(const int32_t* count, int32_t nb, int32_t qpw, int32_t bh_count,
                               int32_t* order, hipStream_t stream);

@@ -32,9 +32,12 @@ class FrozenLists:
     was built with, and a launch plan made on first use.
     """
 
-    def __init__(self, block: int = 64, threshold: float = 0.99):
+    def __init__(self, block: int = 64, threshold: float = 0.99, max_workspace_bytes=None):
         self.block = int(block)
         self.threshold = threshold
+        # cap on the construction step's workspace (None: the full size, one
+        # pass over every head); a smaller one costs more passes, not results
+        self.max_workspace_bytes = max_workspace_bytes
         self._layers = {}
 
     # ------------------------------------------------------------ contents
@@ -81,7 +84,8 @@ class FrozenLists:
         ``o`` of this step."""
         tau = self.threshold if threshold is None else threshold
         o, _, mass = api.dense_attn_mass(q, k, v, block=self.block, o=o, want_lse=False,
-                                         workspace=workspace)
+                                         workspace=workspace,
+                                         max_workspace_bytes=self.max_workspace_bytes)
         if torch.is_tensor(tau):
             idx, count = api.select_per_row(mass, tau, rows_per_threshold or 1)
             tau_meta = "per-row"

@@ -154,16 +154,22 @@ losa_status losa_block_mass_noalloc(const losa_attn_desc* desc, const void* q, c
  * equals the two-pass result up to rounding.
  * o: output [B,H,N,D]; lse: output [B,H,N] fp32 or NULL; mass: output
  * [B,H,nb,nb] fp32.
- * workspace: device memory of at least losa_dense_attn_mass_workspace(desc)
- *   bytes, 256-byte aligned, owned by the caller; its contents on entry are
- *   ignored and on return are unspecified (4*B*H*N*(nb+1) bytes plus
- *   alignment: 0.8 GB for B1 H12 N32760 block 64).  Calls running at the
- *   same time need separate workspaces.
+ * workspace: device memory, 256-byte aligned, owned by the caller; its
+ *   contents on entry are ignored and on return are unspecified.  With
+ *   losa_dense_attn_mass_workspace(desc) bytes (4*B*H*N*(nb+1) plus
+ *   alignment: 0.8 GB for B1 H12 N32760 block 64, 10.6 GB for B1 H24
+ *   N118800 block 128) every (b, h) runs in one pass.  Any smaller size of
+ *   at least losa_dense_attn_mass_workspace_min(desc) bytes (one (b, h):
+ *   4*N*(nb+1) plus alignment, 67 MB and 442 MB for those two shapes) is
+ *   also accepted: the call then makes several passes, each over as many
+ *   heads of one batch item as the workspace holds, with the same results
+ *   bit for bit.  Calls running at the same time need separate workspaces.
  * For LOSA_FP32 the call runs the dense pass and the two-pass mass kernel
  * (the workspace then holds lse when lse is NULL).
- * Returns LOSA_ERR_WORKSPACE when workspace_bytes is below the requirement.
+ * Returns LOSA_ERR_WORKSPACE when workspace_bytes is below the minimum.
  */
 int64_t losa_dense_attn_mass_workspace(const losa_attn_desc* desc);
+int64_t losa_dense_attn_mass_workspace_min(const losa_attn_desc* desc);
 losa_status losa_dense_attn_mass(const losa_attn_desc* desc, const void* q, const void* k,
                                  const void* v, void* o, float* lse, float* mass,
                                  void* workspace, int64_t workspace_bytes, void* stream);
@@ -257,22 +263,27 @@ losa_status losa_sparse_attn(const losa_attn_desc* desc, const void* q, const vo
  * bytes, 4-byte aligned, caller-owned) from count [B,H,nb]; only count is
  * read.  Recompute it whenever count changes.  Returns LOSA_ERR_WORKSPACE
  * when plan_bytes is below the size.  Items of equal cost may be ordered
- * differently from call to call; results do not depend on the order.
+ * differently from call to call; results do not depend on the order.  The
+ * plan opens with a header naming the shape it was made for (work items,
+ * nb, query blocks per item).
  * losa_sparse_attn_planned computes exactly what losa_sparse_attn computes
- * (bit-identical outputs) in the plan's order.  The plan must hold at
- * least losa_sparse_plan_size(desc) bytes (the kernel reads one entry per
- * workgroup it launches; its size is not passed, so this is the caller's
- * guarantee) and should come from losa_sparse_plan for the same desc: a
- * plan made from other counts of the same shape is still a complete order,
- * only a slower one; entries outside the valid range are skipped, leaving
- * those rows unwritten.  For LOSA_FP32 the plan is ignored.
+ * (bit-identical outputs) in the plan's order.  plan_bytes below
+ * losa_sparse_plan_size(desc) returns LOSA_ERR_WORKSPACE (nothing
+ * launched).  A plan whose header names another shape is not followed: the
+ * kernel then runs the work items in index order, so the results are still
+ * complete and correct, only the launch is slower.  A plan made from other
+ * counts of the same shape is still a complete order, only a slower one.
+ * Slot entries are trusted: an entry outside the valid range (a plan
+ * overwritten by the caller) is skipped, leaving its rows unwritten.  For
+ * LOSA_FP32 the plan is ignored.
  */
 int64_t losa_sparse_plan_size(const losa_attn_desc* desc);
 losa_status losa_sparse_plan(const losa_attn_desc* desc, const int32_t* count, int32_t* plan,
                              int64_t plan_bytes, void* stream);
 losa_status losa_sparse_attn_planned(const losa_attn_desc* desc, const void* q, const void* k,
                                      const void* v, const int32_t* idx, const int32_t* count,
-                                     const int32_t* plan, void* o, float* lse, void* stream);
+                                     const int32_t* plan, int64_t plan_bytes, void* o,
+                                     float* lse, void* stream);
 
 /* Static text for a status code. */
 const char* losa_status_string(losa_status status);

@@ -136,8 +136,15 @@ def test_dense_attn_mass_workspace_and_validation(lib):
     rowsum = 4 * 12 * 512 * 32760
     assert need == (rowsum + 255) // 256 * 256 + 4 * 12 * 32760
     assert lib.losa_dense_attn_mass_workspace(None) == -1
+    # the least it takes: one (b, h) per pass
+    least = lib.losa_dense_attn_mass_workspace_min(d)
+    assert least == (4 * 512 * 32760 + 255) // 256 * 256 + 4 * 32760
+    assert lib.losa_dense_attn_mass_workspace_min(None) == -1
+    assert lib.losa_dense_attn_mass_workspace_min(desc(head_dim=96)) == -1
     args = [FAKE, FAKE, FAKE, FAKE, NULL, FAKE]
-    assert lib.losa_dense_attn_mass(d, *args, FAKE, need - 1, NULL) == 8
+    assert lib.losa_dense_attn_mass(d, *args, FAKE, least - 1, NULL) == 8
+    assert lib.losa_dense_attn_mass(d, *args, FAKE, 0, NULL) == 8
+    assert lib.losa_dense_attn_mass(d, *args, FAKE, -1, NULL) == 8
     assert lib.losa_dense_attn_mass(d, *args, NULL, need, NULL) == 1
     assert lib.losa_dense_attn_mass(d, FAKE, FAKE, FAKE, FAKE, NULL, NULL, FAKE, need, NULL) == 1
     assert lib.losa_dense_attn_mass(d, *args, ctypes.c_void_p(0x10010), need, NULL) == 5
@@ -179,11 +186,13 @@ def test_per_row_select_mask_and_retained_validation(lib):
 
 def test_sparse_plan_validation(lib):
     d = desc(batch=1, heads=12, seq_len=32760, block=64)
-    # one slot per 128-row work item, padded to whole rounds of 8 runs of 8
-    assert lib.losa_sparse_plan_size(d) == 4 * 12 * 256
-    assert lib.losa_sparse_plan_size(desc(seq_len=118800, block=128, heads=24)) == 4 * 22336
+    # a 4-word header, then one slot per 128-row work item, padded to whole
+    # rounds of 8 runs of 8
+    assert lib.losa_sparse_plan_size(d) == 4 * (4 + 12 * 256)
+    assert lib.losa_sparse_plan_size(desc(seq_len=118800, block=128, heads=24)) == \
+        4 * (4 + 22336)
     assert lib.losa_sparse_plan_size(desc(batch=2, heads=48, seq_len=17776, head_dim=64)) \
-        == 4 * 64 * ((2 * 48 * 139 + 63) // 64)
+        == 4 * (4 + 64 * ((2 * 48 * 139 + 63) // 64))
     assert lib.losa_sparse_plan_size(None) == -1
     need = lib.losa_sparse_plan_size(d)
     assert lib.losa_sparse_plan(d, NULL, FAKE, need, NULL) == 1
@@ -192,11 +201,15 @@ def test_sparse_plan_validation(lib):
     assert lib.losa_sparse_plan(d, FAKE, FAKE, need - 4, NULL) == 8
     assert lib.losa_sparse_plan(desc(block=32), FAKE, FAKE, need, NULL) == 2
     args = [FAKE, FAKE, FAKE, FAKE, FAKE]
-    assert lib.losa_sparse_attn_planned(d, *args, NULL, FAKE, NULL, NULL) == 1
-    assert lib.losa_sparse_attn_planned(d, *args, ctypes.c_void_p(0x10002), FAKE, NULL,
+    assert lib.losa_sparse_attn_planned(d, *args, NULL, need, FAKE, NULL, NULL) == 1
+    assert lib.losa_sparse_attn_planned(d, *args, ctypes.c_void_p(0x10002), need, FAKE, NULL,
                                         NULL) == 5
-    assert lib.losa_sparse_attn_planned(d, *args, FAKE, NULL, NULL, NULL) == 1
-    assert lib.losa_sparse_attn_planned(desc(head_dim=96), *args, FAKE, FAKE, NULL, NULL) == 2
+    assert lib.losa_sparse_attn_planned(d, *args, FAKE, need, NULL, NULL, NULL) == 1
+    assert lib.losa_sparse_attn_planned(desc(head_dim=96), *args, FAKE, need, FAKE, NULL,
+                                        NULL) == 2
+    # a plan shorter than the shape's plan size is refused before any launch
+    assert lib.losa_sparse_attn_planned(d, *args, FAKE, need - 4, FAKE, NULL, NULL) == 8
+    assert lib.losa_sparse_attn_planned(d, *args, FAKE, 0, FAKE, NULL, NULL) == 8
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):

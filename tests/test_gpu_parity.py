@@ -76,14 +76,17 @@ CASES = {
 
 
 def _check_plan(plan, count, blk):
-    """A plan places every work item (one per 128 query rows of each (b, h))
-    exactly once; read in rank order (runs of 8 ranks per XCD, dealt to the 8
-    XCDs in turn), the cost buckets never rise and items of one bucket keep
-    their index order.  Unused slots hold -1."""
+    """A plan opens with a header naming its shape (magic, work items, nb,
+    query blocks per item), then places every work item (one per 128 query
+    rows of each (b, h)) exactly once; read in rank order (runs of 8 ranks
+    per XCD, dealt to the 8 XCDs in turn), the cost buckets never rise and
+    items of one bucket keep their index order.  Unused slots hold -1."""
     b, h, nb = count.shape
     qpw = 2 if blk == 64 else 1
     wph = (nb + qpw - 1) // qpw
     n = b * h * wph
+    assert plan[:4].tolist() == [0x41536F4C, n, nb, qpw]
+    plan = plan[4:]
     assert np.array_equal(np.sort(plan[plan >= 0]), np.arange(n))
     assert (plan[plan < 0] == -1).all()
     ch, xcds = 8, 8
@@ -415,3 +418,35 @@ def test_scale_argument(losa):
         od, lsed = oracle.dense_attention(q[0, h], k[0, h], v[0, h], scale=0.05)
         _compare_attention(_np(o)[0, h], _np(lse)[0, h], od, lsed, f"scale h{h}")
     assert math.isfinite(float(lse.float().abs().max()))
+
+
+def test_plan_of_another_shape_is_not_followed(losa):
+    """A plan made for another shape with the same number of slots (8 work
+    items of two heads against 12 of three, both 64 slots) passes the size
+    check; its header names the other shape, so the kernel runs every work
+    item in index order instead of the plan's slots: the same bits as the
+    unplanned call, every row written, within the bounds of the oracle."""
+    cfg = synth.small_config(n_grid=(4, 8, 15), head_dim=128, block=64, heads=3,
+                             alpha=(2.0, 0.5, 3.0), seed=41)
+    nb = cfg.num_blocks
+    assert nb == 8
+    _say("[parity] plan of another shape")
+    q, k, v = synth.make_inputs(cfg)
+    tq, tk, tv = (_dev(x, "bf16") for x in (q, k, v))
+    mass = losa.block_mass(tq, tk, block=64)
+    idx, cnt = losa.select(mass, 0.9)
+    plan3 = losa.sparse_plan(cnt, block=64, head_dim=128)
+    plan2 = losa.sparse_plan(cnt[:, :2].contiguous(), block=64, head_dim=128)
+    assert plan2.numel() == plan3.numel()
+    o_u, l_u = losa.sparse_attn(tq, tk, tv, idx, cnt, block=64, want_lse=True)
+    o_p, l_p = losa.sparse_attn(tq, tk, tv, idx, cnt, block=64, want_lse=True, plan=plan3)
+    o_w = torch.full_like(o_u, float("nan"))
+    l_w = torch.full_like(l_u, float("nan"))
+    losa.sparse_attn(tq, tk, tv, idx, cnt, block=64, o=o_w, lse=l_w, plan=plan2)
+    torch.cuda.synchronize()
+    assert torch.equal(o_p, o_u) and torch.equal(l_p, l_u)
+    assert torch.equal(o_w, o_u) and torch.equal(l_w, l_u)
+    og, lg, ig, cg = _np(o_w), _np(l_w), _np(idx), _np(cnt)
+    for h in range(cfg.heads):
+        ro, rl = oracle.sparse_attention(q[0, h], k[0, h], v[0, h], ig[0, h], cg[0, h], 64)
+        _compare_attention(og[0, h], lg[0, h], ro, rl, f"foreign plan h{h}")
