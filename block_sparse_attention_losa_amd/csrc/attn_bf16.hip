@@ -81,7 +81,7 @@ struct GeoB {
 // loop is bound by the softmax VALU work rather than the matrix cores, and a
 // third wave per SIMD (168 VGPRs, a few spilled values reloaded per step)
 // hides more of its latency: measured 3-4 % faster than two waves.
-template <int D, int BLK, int MODE, int ROWS>
+template <int D, int BLK, int MODE, int ROWS, bool MFSUM>
 __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 2)))
     attn_bf16_kernel(AttnParams p) {
   using G = GeoB<D, BLK, MODE, ROWS>;
@@ -207,6 +207,28 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   float m_thr = -INFINITY;  // m_run + kRaise: a tile whose scaled max passes it raises m_run
   float m_use = 0.f;        // m_run, or 0 while it is -inf (no finite score yet)
   float l_run = 0.f;        // this lane's partial row sum
+  // Row sums on the matrix cores (dense and sparse attention when no lse is
+  // asked for): the probabilities are rounded to bf16 for the P V product
+  // anyway, and summing exactly those values on a 16x16x32 MFMA takes 32
+  // VALU adds per tile off the softmax, the bottleneck at D = 64 (measured
+  // 2-3 % faster there, 0.5-1.5 % at D = 128).  O is then normalised by the
+  // sum of the very weights it averages V with.  lse needs the unrounded sum
+  // (a bf16 probability is off by up to 2^-9 of itself), so when lse is
+  // written the adds stay on the VALU in fp32.  The A operand selects, for
+  // output row 4*(lane/16), the two lane groups that hold this lane's query
+  // row in the B-operand layout of the P V product (lanes q and q + 32), so
+  // register 0 of every lane accumulates its own row's full sum.
+  constexpr bool kMfmaSum = MFSUM && (MODE == kDense || MODE == kSparse);
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 rowsel;
+  {
+    const int r16 = lane & 15, kg = lane >> 4;
+    const bool one = ((r16 == 0 || r16 == 8) && (kg & 1) == 0) ||
+                     ((r16 == 4 || r16 == 12) && (kg & 1) == 1);
+    const unsigned wv = one ? 0x3F803F80u : 0u;  // bf16 1.0 in both halves
+    const u32x4 w4 = {wv, wv, wv, wv};
+    rowsel = __builtin_bit_cast(bf16x8, w4);
+  }
   const float c2 = p.scale * kLog2e;
   float lse_row = 0.f;      // kMass: the row's lse in log2 units, +inf on padding rows
   float tacc = 0.f;         // kDenseMass: current key block's share of the row sum
@@ -356,21 +378,27 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[mt][i] *= alpha;
         }
+        if constexpr (kMfmaSum) lacc[0] *= alpha;
       }
       if constexpr (kInline) compute_s(nslot, sn);
       const float m_e = keep ? m_use : INFINITY;
+      // with the row sums on the matrix cores the exponentials are taken
+      // where the P V product packs them (fewer live registers: at D = 64
+      // this removes the loop's spills)
       float pr[2][16];
       float lsum = 0.f;
+      if constexpr (!kMfmaSum) {
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
+        for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          pr[cc][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][i], c2, -m_e));
-          lsum += pr[cc][i];
-        }
-      // alpha is 1 unless the wave raised, and fma(l, 1, x) rounds exactly
-      // like l + x
-      l_run = __builtin_fmaf(l_run, alpha, lsum);
+          for (int i = 0; i < 16; ++i) {
+            pr[cc][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][i], c2, -m_e));
+            lsum += pr[cc][i];
+          }
+        // alpha is 1 unless the wave raised, and fma(l, 1, x) rounds exactly
+        // like l + x
+        l_run = __builtin_fmaf(l_run, alpha, lsum);
+      }
       if constexpr (MODE == kDenseMass) {
         // the tile's part of the row sum (both lanes of the row), against
         // the current reference and accumulated over the key block's tiles;
@@ -395,11 +423,19 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             u32x4 pk;
-            pk[0] = pack_bf16x2(pr[cc][8 * h + 0], pr[cc][8 * h + 1]);
-            pk[1] = pack_bf16x2(pr[cc][8 * h + 2], pr[cc][8 * h + 3]);
-            pk[2] = pack_bf16x2(pr[cc][8 * h + 4], pr[cc][8 * h + 5]);
-            pk[3] = pack_bf16x2(pr[cc][8 * h + 6], pr[cc][8 * h + 7]);
+            if constexpr (kMfmaSum) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                pk[j] = pack_bf16x2(
+                    __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][8 * h + 2 * j], c2, -m_e)),
+                    __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][8 * h + 2 * j + 1], c2, -m_e)));
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                pk[j] = pack_bf16x2(pr[cc][8 * h + 2 * j], pr[cc][8 * h + 2 * j + 1]);
+            }
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
+            if constexpr (kMfmaSum) lacc = mfma16_bf16(rowsel, pb, lacc);
 #pragma unroll
             for (int mt = 0; mt < kORegs; ++mt) {
               const bf16x8 a = v_operand(vs, cc * 32 + h * 16 + g * 8, mt);
@@ -574,7 +610,8 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
     return;
   } else {
     flush_rowsum();
-    const float l_tot = pair_sum(l_run);
+    // (the matrix-core sum already holds both halves of the row)
+    const float l_tot = kMfmaSum ? lacc[0] : pair_sum(l_run);
     if (!row_ok) return;
     const bool empty = !(l_tot > 0.f);
     if (p.lse != nullptr && g == 0) {
@@ -602,10 +639,10 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   }
 }
 
-template <int D, int BLK, int MODE, int ROWS = 128>
+template <int D, int BLK, int MODE, int ROWS = 128, bool MFSUM = false>
 hipError_t launch_b(const AttnParams& p, hipStream_t stream) {
   using G = GeoB<D, BLK, MODE, ROWS>;
-  auto kern = attn_bf16_kernel<D, BLK, MODE, ROWS>;
+  auto kern = attn_bf16_kernel<D, BLK, MODE, ROWS, MFSUM>;
   static std::atomic<bool> lds_set[kMaxDevices];
   const hipError_t attr = set_lds_limit(kern, G::kLdsBytes, lds_set);
   if (attr != hipSuccess) return attr;
@@ -619,8 +656,15 @@ hipError_t launch_b(const AttnParams& p, hipStream_t stream) {
 template <int D, int BLK>
 hipError_t launch_b_mode(int mode, const AttnParams& p, hipStream_t stream) {
   switch (mode) {
-    case kDense: return launch_b<D, BLK, kDense, attn_rows(kDense, D, BLK)>(p, stream);
-    case kSparse: return launch_b<D, BLK, kSparse, attn_rows(kSparse, D, BLK)>(p, stream);
+    // without an lse output the row sums go to the matrix cores
+    case kDense:
+      return p.lse == nullptr
+                 ? launch_b<D, BLK, kDense, attn_rows(kDense, D, BLK), true>(p, stream)
+                 : launch_b<D, BLK, kDense, attn_rows(kDense, D, BLK)>(p, stream);
+    case kSparse:
+      return p.lse == nullptr
+                 ? launch_b<D, BLK, kSparse, attn_rows(kSparse, D, BLK), true>(p, stream)
+                 : launch_b<D, BLK, kSparse, attn_rows(kSparse, D, BLK)>(p, stream);
     case kLse: return launch_b<D, BLK, kLse>(p, stream);
     case kMass: return launch_b<D, BLK, kMass>(p, stream);
     case kDenseMass: return launch_b<D, BLK, kDenseMass, attn_rows(kDenseMass, D, BLK)>(p, stream);

@@ -7,7 +7,7 @@
 #include <cstdint>
 #include <cstring>
 
-#include "../../include/losa.h"
+#include "losa.h"
 #include "losa_launch.h"
 
 namespace {

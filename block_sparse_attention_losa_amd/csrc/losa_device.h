@@ -9,6 +9,7 @@ namespace losa {
 typedef __bf16 bf16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
 
@@ -20,6 +21,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 // register i of lane l holds D[8*(i/4) + 4*(l/32) + i%4][l%32].
 __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16 output tile, bf16 inputs with 32-deep contraction: D = A * B + C.
+// Lane l supplies A[l%16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l%16];
+// register i of lane l holds D[4*(l/16) + i][l%16].
+__device__ __forceinline__ f32x4 mfma16_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // Same output tile, fp32 inputs with a 2-deep contraction: lane l supplies

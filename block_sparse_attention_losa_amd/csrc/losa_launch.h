@@ -6,7 +6,7 @@
 
 #include <atomic>
 
-#include "../../include/losa.h"
+#include "losa.h"
 
 namespace losa {
 

@@ -9,7 +9,7 @@
 #include <cstdint>
 #include <mutex>
 
-#include "../../include/losa.h"
+#include "losa.h"
 #include "losa_launch.h"
 
 namespace {

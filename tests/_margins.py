@@ -19,6 +19,11 @@ def record(test, case, **values):
         return
     row = {"test": test, "case": case}
     for key, val in values.items():
-        row[key] = float(val) if hasattr(val, "__float__") and not isinstance(val, bool) else val
+        if isinstance(val, bool) or not hasattr(val, "__float__"):
+            row[key] = val
+        elif float(val).is_integer() and "int" in type(val).__name__:
+            row[key] = int(val)
+        else:
+            row[key] = float(val)
     with _lock, open(path, "a") as fh:
         fh.write(json.dumps(row) + "\n")

@@ -173,11 +173,15 @@ def _run_config(losa, cid, taus, later_step=None, seed=0, cfg=None):
         so, slse = losa.sparse_attn(sq, sk, sv, idx, cnt, block=blk, want_lse=True)
         plan = losa.sparse_plan(cnt, block=blk, head_dim=cfg.head_dim)
         sop, slsep = losa.sparse_attn(sq, sk, sv, idx, cnt, block=blk, want_lse=True, plan=plan)
+        # the benchmark's call: planned, no lse (row sums on the matrix cores)
+        son, _ = losa.sparse_attn(sq, sk, sv, idx, cnt, block=blk, plan=plan)
         torch.cuda.synchronize()
         assert torch.equal(sop, so) and torch.equal(slsep, slse), (cid, tau, "planned")
         del sop, slsep
         idx_g, cnt_g = idx.cpu().numpy(), cnt.cpu().numpy()
         so_g, slse_g = so.float().cpu().numpy(), slse.cpu().numpy()
+        son_g = son.float().cpu().numpy()
+        del son
         if later_step is not None:
             qh, kh, vh = (x.float().cpu().numpy() for x in (sq, sk, sv))
         _check_selection_properties(mass_g, idx_g, cnt_g, tau)
@@ -222,7 +226,9 @@ def _run_config(losa, cid, taus, later_step=None, seed=0, cfg=None):
             ro, rl = oracle.sparse_attention(qh[b, h], kh[b, h], vh[b, h], idx_g[b, h],
                                              cnt_g[b, h], blk, qblocks=qbs)
             err = np.abs(so_g[b, h, rows_].astype(np.float64) - ro)
+            errn = np.abs(son_g[b, h, rows_].astype(np.float64) - ro)
             out = {"o_max": err.max(), "o_mean": err.mean(),
+                   "nolse_o_max": errn.max(), "nolse_o_mean": errn.mean(),
                    "lse_err": slse_g[b, h, rows_] - rl}
             if later_step is not None:
                 # the dense lse of the later step, and the retained mass it
@@ -239,9 +245,13 @@ def _run_config(losa, cid, taus, later_step=None, seed=0, cfg=None):
         sres = dict(zip(pairs, _per_head(sparse, pairs)))
         s_worst = {"o_max": max(r["o_max"] for r in sres.values()),
                    "o_mean": max(r["o_mean"] for r in sres.values()),
+                   "nolse_o_max": max(r["nolse_o_max"] for r in sres.values()),
+                   "nolse_o_mean": max(r["nolse_o_mean"] for r in sres.values()),
                    "lse": max(float(np.abs(r["lse_err"]).max()) for r in sres.values())}
         for bh, r in sres.items():
             assert r["o_max"] <= O_MAX and r["o_mean"] <= O_MEAN, (cid, tau, bh, r["o_max"])
+            assert r["nolse_o_max"] <= O_MAX and r["nolse_o_mean"] <= O_MEAN, \
+                (cid, tau, bh, "no lse", r["nolse_o_max"])
             assert np.abs(r["lse_err"]).max() <= LSE_ATOL, (cid, tau, bh)
         extra = {}
         if later_step is not None:

@@ -199,11 +199,13 @@ def test_registry_matches_oracle_and_direct_calls(losa, tmp_path):
     o_ref, _, mass = losa.dense_attn_mass(q, k, v, block=64)
     idx, cnt = losa.select(mass, 0.95)
     o1, l1 = reg.attend("blocks.0.attn", lq, lk, lv, want_lse=True)
-    o1_ref, _ = losa.sparse_attn(lq, lk, lv, idx, cnt, block=64)
+    o1_ref, _ = losa.sparse_attn(lq, lk, lv, idx, cnt, block=64, want_lse=True)
+    o1n, _ = reg.attend("blocks.0.attn", lq, lk, lv)
+    o1n_ref, _ = losa.sparse_attn(lq, lk, lv, idx, cnt, block=64)
     torch.cuda.synchronize()
     ridx, rcnt = reg.lists("blocks.0.attn")
     ri_g, rc_g, m_g = _np(ridx), _np(rcnt), _np(mass)
-    o_g, o1_g, l1_g = _np(o_c), _np(o1), _np(l1)
+    o_g, o1_g, l1_g, o1n_g = _np(o_c), _np(o1), _np(l1), _np(o1n)
     for h in range(cfg.heads):
         # construction step: the dense output and the lists against the oracle
         od, lsed = oracle.dense_attention(qn[0, h], kn[0, h], vn[0, h])
@@ -218,6 +220,7 @@ def test_registry_matches_oracle_and_direct_calls(losa, tmp_path):
         so, sl = oracle.sparse_attention(lqn[0, h], lkn[0, h], lvn[0, h], ri_g[0, h],
                                          rc_g[0, h], 64)
         _attn_err(o1_g[0, h], l1_g[0, h], so, sl, f"registry attend h{h}")
+        _attn_err(o1n_g[0, h], None, so, sl, f"registry attend no-lse h{h}")
     # the registry reproduces the direct calls
     assert torch.equal(o_c, o_ref)
     assert torch.equal(rcnt, cnt)
@@ -225,7 +228,7 @@ def test_registry_matches_oracle_and_direct_calls(losa, tmp_path):
         b_, h_, i_ = np.unravel_index(flat, tuple(cnt.shape))
         c = int(cnt[b_, h_, i_])
         assert torch.equal(ridx[b_, h_, i_, :c], idx[b_, h_, i_, :c])
-    assert torch.equal(o1, o1_ref)
+    assert torch.equal(o1, o1_ref) and torch.equal(o1n, o1n_ref)
     assert torch.equal(reg.mask("blocks.0.attn"), losa.block_mask(idx, cnt))
     ret = reg.retained_mass("blocks.0.attn", lq, lk, lv)
     assert ret.shape == (1, 2, nb) and float(ret.min()) >= 0.0

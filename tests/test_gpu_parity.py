@@ -145,7 +145,10 @@ def test_pipeline_matches_oracle(losa, name):
     mass_own = losa.block_mass(tq, tk, block=blk)  # first pass inside
     _say(f"[parity] {name}: dense_attn_mass")
     o_f, lse_f, mass_f = losa.dense_attn_mass(tq, tk, tv, block=blk)
+    # without an lse output (bf16: row sums on the matrix cores)
+    o_n, _ = losa.dense_attn(tq, tk, tv, block=blk, want_lse=False)
     torch.cuda.synchronize()
+    o_ng = _np(o_n)
     o_g, lse_g, mass_g = _np(o), _np(lse), _np(mass)
     assert np.array_equal(mass_g, _np(mass_own)) or np.abs(mass_g - _np(mass_own)).max() < 1e-7
     # the one-sweep construction: O and lse from the dense pass's own
@@ -160,6 +163,8 @@ def test_pipeline_matches_oracle(losa, name):
             od, lsed = oracle.dense_attention(q[b, h], k[b, h], v[b, h])
             worst.add("dense_", _compare_attention(o_g[b, h], lse_g[b, h], od, lsed,
                                                    f"{name} dense b{b}h{h}"))
+            worst.add("dense_nolse_", _compare_attention(o_ng[b, h], None, od, None,
+                                                         f"{name} dense no-lse b{b}h{h}"))
             md = oracle.block_mass(q[b, h], k[b, h], blk, lse=lsed)
             merr = np.abs(mass_g[b, h].astype(np.float64) - md).max()
             assert merr <= MASS_ATOL, f"{name} mass b{b}h{h} err {merr:.3e}"
@@ -176,10 +181,15 @@ def test_pipeline_matches_oracle(losa, name):
         # the planned launch (work items longest-first) gives the same bits
         plan = losa.sparse_plan(count, block=blk)
         op_, lsep = losa.sparse_attn(tq, tk, tv, idx, count, block=blk, want_lse=True, plan=plan)
+        # and without lse, planned and not (the benchmark's call)
+        on_, _ = losa.sparse_attn(tq, tk, tv, idx, count, block=blk, plan=plan)
+        onu, _ = losa.sparse_attn(tq, tk, tv, idx, count, block=blk)
         torch.cuda.synchronize()
         assert torch.equal(op_, os_) and torch.equal(lsep, lses), f"{name} planned tau={tau}"
+        assert torch.equal(on_, onu), f"{name} planned no-lse tau={tau}"
         _check_plan(plan.cpu().numpy(), count.cpu().numpy(), blk)
         idx_g, cnt_g, os_g, lses_g = _np(idx), _np(count), _np(os_), _np(lses)
+        on_g = _np(on_)
         for b in range(cfg.batch):
             for h in range(cfg.heads):
                 ridx, rcnt = oracle.select(mass_g[b, h], tau)
@@ -193,11 +203,14 @@ def test_pipeline_matches_oracle(losa, name):
                 worst.add("sparse_", _compare_attention(os_g[b, h], lses_g[b, h], ref_o,
                                                         ref_lse,
                                                         f"{name} sparse tau={tau} b{b}h{h}"))
+                worst.add("sparse_nolse_", _compare_attention(
+                    on_g[b, h], None, ref_o, None, f"{name} sparse no-lse tau={tau} b{b}h{h}"))
         if tau == 1.0:
             # every block kept, visited in the same ascending order as the
             # dense pass: the two kernels do identical arithmetic
             assert (cnt_g == nb).all()
             assert np.array_equal(os_g, o_g) and np.array_equal(lses_g, lse_g)
+            assert np.array_equal(on_g, o_ng)
     _margins.record("parity", name, **worst.v)
 
 
@@ -240,9 +253,12 @@ def test_ragged_tail_sweep(losa, d, blk, tail):
     idx, cnt = losa.select(mass, 0.9)
     plan = losa.sparse_plan(cnt, block=blk, head_dim=d)
     so, slse = losa.sparse_attn(tq, tk, tv, idx, cnt, block=blk, want_lse=True, plan=plan)
+    sn, _ = losa.sparse_attn(tq, tk, tv, idx, cnt, block=blk, plan=plan)
+    dn, _ = losa.dense_attn(tq, tk, tv, block=blk, want_lse=False)
     torch.cuda.synchronize()
     o_g, lse_g, mass_g = _np(o), _np(lse), _np(mass)
     idx_g, cnt_g, so_g, slse_g = _np(idx), _np(cnt), _np(so), _np(slse)
+    sn_g, dn_g = _np(sn), _np(dn)
     for h in range(cfg.heads):
         od, lsed = oracle.dense_attention(q[0, h], k[0, h], v[0, h])
         _compare_attention(o_g[0, h], lse_g[0, h], od, lsed, f"tail N={n} dense h{h}")
@@ -256,6 +272,8 @@ def test_ragged_tail_sweep(losa, d, blk, tail):
         ref_o, ref_lse = oracle.sparse_attention(q[0, h], k[0, h], v[0, h], idx_g[0, h],
                                                  cnt_g[0, h], blk)
         _compare_attention(so_g[0, h], slse_g[0, h], ref_o, ref_lse, f"tail N={n} sparse h{h}")
+        _compare_attention(sn_g[0, h], None, ref_o, None, f"tail N={n} sparse no-lse h{h}")
+        _compare_attention(dn_g[0, h], None, od, None, f"tail N={n} dense no-lse h{h}")
 
 
 @pytest.mark.parametrize("d,blk,dtype", [(128, 64, "bf16"), (64, 128, "bf16"),
@@ -279,18 +297,21 @@ def test_sparse_arbitrary_lists(losa, d, blk, dtype):
     idx[0, 1, 1, :2], cnt[0, 1, 1] = [nb - 1, 0], 2
     cnt[0, 1, nb - 1] = 0                               # empty list
     tq, tk, tv = (_dev(x, dtype) for x in (q, k, v))
-    o, lse = losa.sparse_attn(tq, tk, tv, torch.from_numpy(idx).cuda(),
-                              torch.from_numpy(cnt).cuda(), block=blk, want_lse=True)
+    ti, tc = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    o, lse = losa.sparse_attn(tq, tk, tv, ti, tc, block=blk, want_lse=True)
+    on, _ = losa.sparse_attn(tq, tk, tv, ti, tc, block=blk)
     torch.cuda.synchronize()
-    o_g, lse_g = _np(o), _np(lse)
+    o_g, lse_g, on_g = _np(o), _np(lse), _np(on)
     for h in range(2):
         qbs = [i for i in range(nb) if cnt[0, h, i] > 0]
         ref_o, ref_lse = oracle.sparse_attention(q[0, h], k[0, h], v[0, h], idx[0, h],
                                                  cnt[0, h], blk, qblocks=qbs)
         rows = np.concatenate([np.arange(i * blk, min(cfg.seq_len, (i + 1) * blk)) for i in qbs])
         _compare_attention(o_g[0, h, rows], lse_g[0, h, rows], ref_o, ref_lse, f"lists h{h}")
+        _compare_attention(on_g[0, h, rows], None, ref_o, None, f"lists no-lse h{h}")
     lo = (nb - 1) * blk
     assert (o_g[0, 1, lo:] == 0).all() and np.isneginf(lse_g[0, 1, lo:]).all()
+    assert (on_g[0, 1, lo:] == 0).all()
 
 
 def _clean_lists(idx, cnt, nb):
@@ -343,9 +364,12 @@ def test_sparse_partner_blocks_and_list_guarantees(losa, d):
     o, lse = losa.sparse_attn(tq, tk, tv, ti, tc, block=64, want_lse=True)
     plan = losa.sparse_plan(tc, block=64, head_dim=d)
     o2, lse2 = losa.sparse_attn(tq, tk, tv, ti, tc, block=64, want_lse=True, plan=plan)
+    on, _ = losa.sparse_attn(tq, tk, tv, ti, tc, block=64)
+    on2, _ = losa.sparse_attn(tq, tk, tv, ti, tc, block=64, plan=plan)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
-    o_g, lse_g = _np(o), _np(lse)
+    assert torch.equal(on, on2)
+    o_g, lse_g, on_g = _np(o), _np(lse), _np(on)
     for h in range(2):
         ci, cc = _clean_lists(idx[0, h], cnt[0, h], nb)
         qbs = [i for i in range(nb) if cc[i] > 0]
@@ -354,10 +378,12 @@ def test_sparse_partner_blocks_and_list_guarantees(losa, d):
         rows = np.concatenate([np.arange(i * 64, min(cfg.seq_len, (i + 1) * 64)) for i in qbs])
         _compare_attention(o_g[0, h, rows], lse_g[0, h, rows], ref_o, ref_lse,
                            f"partner lists d={d} h{h}")
+        _compare_attention(on_g[0, h, rows], None, ref_o, None, f"partner lists no-lse d={d} h{h}")
         for i in range(nb):
             if cc[i] == 0:
                 r = slice(i * 64, min(cfg.seq_len, (i + 1) * 64))
                 assert (o_g[0, h, r] == 0).all() and np.isneginf(lse_g[0, h, r]).all(), (h, i)
+                assert (on_g[0, h, r] == 0).all(), (h, i)
 
 
 @pytest.mark.parametrize("nkb", [1, 3, 16, 64, 65, 200, 512, 929, 1024])

@@ -54,18 +54,23 @@ def test_two_streams_match_sequential(losa):
     steps = [_inputs(t) for t in (4, 5)]
     _say("[streams] sequential reference")
     ref = [losa.sparse_attn(*x, idx, cnt, block=blk, want_lse=True, plan=plan) for x in steps]
+    refn = [losa.sparse_attn(*x, idx, cnt, block=blk, plan=plan)[0] for x in steps]
     torch.cuda.synchronize()
     ref = [(o.clone(), l.clone()) for o, l in ref]
+    refn = [o.clone() for o in refn]
     _say("[streams] two streams at once")
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
-    outs = []
+    outs, outn = [], []
     torch.cuda.synchronize()
     for s, x in zip(streams, steps):
         with torch.cuda.stream(s):
             outs.append(losa.sparse_attn(*x, idx, cnt, block=blk, want_lse=True, plan=plan))
+            outn.append(losa.sparse_attn(*x, idx, cnt, block=blk, plan=plan)[0])
     torch.cuda.synchronize()
     for (o, l), (ro, rl) in zip(outs, ref):
         assert torch.equal(o, ro) and torch.equal(l, rl)
+    for o, ro in zip(outn, refn):
+        assert torch.equal(o, ro)
 
 
 def test_graph_replays_match_eager(losa):
@@ -86,6 +91,7 @@ def test_graph_replays_match_eager(losa):
     plan = losa.sparse_plan(torch.zeros((b, h, nb), dtype=torch.int32, device=dev), block=blk,
                             head_dim=d)
     so = torch.empty_like(q0)
+    so2 = torch.empty_like(q0)
     slse = torch.empty((b, h, n), dtype=torch.float32, device=dev)
 
     def construction():
@@ -95,6 +101,7 @@ def test_graph_replays_match_eager(losa):
 
     def sparse():
         losa.sparse_attn(sq, sk, sv, idx, cnt, block=blk, o=so, lse=slse, plan=plan)
+        losa.sparse_attn(sq, sk, sv, idx, cnt, block=blk, o=so2, plan=plan)  # no lse
 
     _say("[graphs] eager warm-up, then capture")
     for x, y in zip((sq, sk, sv), (q0, k0, v0)):
@@ -118,15 +125,16 @@ def test_graph_replays_match_eager(losa):
         g_con.replay()
         g_sp.replay()
         torch.cuda.synchronize()
-        got = [y.clone() for y in (o, lse, mass, cnt, so, slse)]
+        got = [y.clone() for y in (o, lse, mass, cnt, so, slse, so2)]
         got_idx = idx.clone()
         # eager calls on the same inputs, into fresh outputs
         eo, else_, emass = losa.dense_attn_mass(*x, block=blk)
         eidx, ecnt = losa.select(emass, 0.95)
         eplan = losa.sparse_plan(ecnt, block=blk, head_dim=d)
         eso, eslse = losa.sparse_attn(*x, eidx, ecnt, block=blk, want_lse=True, plan=eplan)
+        eso2, _ = losa.sparse_attn(*x, eidx, ecnt, block=blk, plan=eplan)
         torch.cuda.synchronize()
-        for a, e in zip(got, (eo, else_, emass, ecnt, eso, eslse)):
+        for a, e in zip(got, (eo, else_, emass, ecnt, eso, eslse, eso2)):
             assert torch.equal(a, e), f"replay {rep}"
         c = ecnt.cpu().numpy()
         gi, ei = got_idx.cpu().numpy(), eidx.cpu().numpy()
