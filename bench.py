@@ -30,21 +30,29 @@ METRIC = "sparse-attn ms/call + MFMA util at Wan2.1-1.3B shape (99% mass); x vs 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_wan13_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_attention_losa_amd", "csrc", f)
+SELECT_COUNTERS_FILE = os.path.join(ROOT, "profiles", "select_kernel_counters.json")
+CSRC = os.path.join(ROOT, "block_sparse_attention_losa_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(CSRC, f)
                   for f in ("attn_bf16.hip", "attn_common.h", "losa_device.h",
                             "losa_launch.h", "frozen_lists.hip")]
+SELECT_SOURCES = [os.path.join(CSRC, f) for f in ("select.hip", "losa_device.h", "losa_launch.h")]
+# MI355X: 256 CUs x 4 SIMDs; a wave64 VALU instruction (fp32 or fp64 at full
+# rate) occupies its SIMD for 4 cycles; nominal clock 2.4 GHz
+SIMDS = 1024
+VALU_CYCLES_PER_INSTR = 4
+CLOCK_GHZ = 2.4
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_hash():
+def kernel_hash(sources=None):
     """Hash of the code of the timed kernel, its launch shapes and its launch
     plan (identifies the build a counter summary was taken on).  Comments
     and whitespace are left out, so editing a comment keeps the summary."""
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in KERNEL_SOURCES if sources is None else sources:
         with open(path, encoding="utf-8") as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -83,6 +91,27 @@ def read_traffic(n_launch_units):
     if rec.get("kernel_sha") != kernel_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+def select_floor_ms(rows, nkb):
+    """Compute floor of the selection kernel for `rows` rows of `nkb` key
+    blocks: the VALU instructions it issues per row (counted with rocprofv3,
+    SQ_INSTS_VALU / rows, for the row length's sort size) at one wave64
+    instruction per 4 cycles on each of the 1024 SIMDs at 2.4 GHz.  None when
+    the committed counter summary is absent or was taken on other sources."""
+    if not os.path.exists(SELECT_COUNTERS_FILE):
+        return None
+    with open(SELECT_COUNTERS_FILE) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_sha") != kernel_hash(SELECT_SOURCES):
+        return None
+    sort_size = 16
+    while sort_size < nkb:
+        sort_size *= 2
+    per_row = rec.get("valu_instructions_per_row", {}).get(str(sort_size))
+    if per_row is None:
+        return None
+    return rows * per_row * VALU_CYCLES_PER_INSTR / SIMDS / (CLOCK_GHZ * 1e9) * 1e3
 
 
 def cpu_baseline(cfg, q, k, v, idx, count, budget_s):
@@ -378,10 +407,13 @@ def main():
     dflops = dense_flops(b, h, n, d)
     dense_mean = float(np.mean(dense_later_ms)) if dense_later_ms else None
     traffic = read_traffic(1)
-    # the selection is HBM-bound: it reads the mass map and writes the lists
+    # the selection reads the mass map and writes the lists (its HBM
+    # roofline), and sorts every row (its VALU floor, from counted
+    # instructions)
     rows = b * h * nb
     select_bytes = 4 * nb * rows + 4 * int(cnt_h.sum()) + 4 * rows
     select_mean = float(np.mean(select_ms))
+    select_floor = select_floor_ms(rows, nb)
     props = torch.cuda.get_device_properties(dev)
 
     out = {
@@ -422,7 +454,10 @@ def main():
         "retained_mass": drift,
         "select": {"ms": round(select_mean, 4), "algorithmic_mb": round(select_bytes / 1e6, 2),
                    "gbps": round(select_bytes / (select_mean * 1e-3) / 1e9, 1),
-                   "hbm_peak_gbps": PEAK_HBM_GBS},
+                   "hbm_peak_gbps": PEAK_HBM_GBS,
+                   "hbm_frac": round(select_bytes / (select_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                   "valu_floor_ms": round(select_floor, 4) if select_floor else None,
+                   "valu_floor_frac": round(select_floor / select_mean, 4) if select_floor else None},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "compute_units": props.multi_processor_count,
                    "memory_gib": round(props.total_memory / 2**30, 1)},

@@ -44,3 +44,22 @@ def test_kept_flops_counts_ragged_blocks():
     full = np.array([[[2, 2]]], np.int32)
     both = np.array([[[[0, 1], [0, 1]]]], np.int32)
     assert bench.kept_flops(full, both, 100, 64, 8) == bench.dense_flops(1, 1, 100, 8)
+
+
+def test_select_floor_from_counted_instructions():
+    """The selection's compute floor: rows x counted VALU instructions per
+    row x 4 cycles over 1024 SIMDs at 2.4 GHz, for the row's sort size, and
+    only while the counter summary matches the kernel's sources."""
+    import json
+    with open(bench.SELECT_COUNTERS_FILE) as fh:
+        rec = json.load(fh)
+    if rec["kernel_sha"] != bench.kernel_hash(bench.SELECT_SOURCES):
+        assert bench.select_floor_ms(20480, 512) is None
+        return
+    per_row = rec["valu_instructions_per_row"]["512"]
+    want = 20480 * per_row * 4 / 1024 / 2.4e9 * 1e3
+    assert abs(bench.select_floor_ms(20480, 512) - want) < 1e-12
+    assert abs(bench.select_floor_ms(20480, 278) - want) < 1e-12     # sort size 512 too
+    assert bench.select_floor_ms(100, 929) == 100 * rec["valu_instructions_per_row"]["1024"] \
+        * 4 / 1024 / 2.4e9 * 1e3
+    assert bench.select_floor_ms(100, 100) is None                  # size 128 not counted
