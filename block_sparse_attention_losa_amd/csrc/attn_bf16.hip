@@ -41,7 +41,12 @@
 //    interleaved with the exponentials; the other 128-row passes issue them
 //    ahead of it at a lower wave priority, so the two waves of a SIMD (from
 //    different workgroups) tend to alternate between the matrix core and
-//    the VALU.
+//    the VALU;
+//  * except at D = 64 without lse and for D = 64 sparse attention ("lean"
+//    passes): there K and V both run one tile ahead, a tile's scores are
+//    computed in its own step, and the 32 registers this saves give four
+//    waves per SIMD instead of three; the lean passes without lse also take
+//    the exponentials speculatively, before the row maxima.
 //
 // Scores are computed transposed, S^T = K Q^T, on 32x32x16 MFMA tiles: a
 // lane then holds one query row and 16 of the 32 keys of a chunk, so row
@@ -75,14 +80,37 @@ struct GeoB {
   static constexpr int kAuxBytes =
       MODE == kSparse ? (2 * kMaxBlocks + 16) * 4 : (MODE == kMass ? 4 * kMaxBlocks * 4 : 0);
   static constexpr int kLdsBytes = kRingBytes + kAuxBytes;
+  // sparse: the union list's flags and entries take one slot per key block
+  // (rounded up to 64), so a short sequence leaves LDS for more workgroups
+  static constexpr int lds_bytes(int nb) {
+    return MODE == kSparse ? kRingBytes + (2 * ((nb + 63) / 64) * 64 + 16) * 4 : kLdsBytes;
+  }
 };
 
-// Two waves per SIMD at D = 128 (the loop needs ~250 VGPRs).  At D = 64 the
-// loop is bound by the softmax VALU work rather than the matrix cores, and a
-// third wave per SIMD (168 VGPRs, a few spilled values reloaded per step)
-// hides more of its latency: measured 3-4 % faster than two waves.
+// The D = 64 passes with a P V product and no lse -- sparse attention (with
+// or without lse) and dense attention without lse -- run "lean": the scores
+// of a tile are computed at the start of its own step instead of one step
+// ahead, which frees the 32 registers of the second score set, and the loop
+// fits 128 VGPRs: four waves per SIMD.  At D = 64 a score carries half the
+// matrix work of D = 128 and the same softmax work, so the loop is bound by
+// latency and VALU issue rather than the matrix cores, and the fourth wave
+// hides more of it than the overlap the score prefetch gave within a wave
+// (sparse, CogVideoX layer: 4-5 % faster than three waves with prefetch; the
+// dense lse pass keeps the prefetch, which spills at 128 VGPRs).
+constexpr bool lean_pass(int d, int mode, bool mfsum) {
+  return d == 64 && (mode == kSparse || (mode == kDense && mfsum));
+}
+
+// Workgroups per CU the register budget is sized for.  Two waves per SIMD at
+// D = 128 (the loop needs ~250 VGPRs); at D = 64 three (168 VGPRs: a third
+// wave hides more of the softmax latency than the registers it costs,
+// measured 3-4 % faster than two), four for the lean passes.
+constexpr int attn_occupancy(int d, int mode, int rows, bool mfsum) {
+  return rows == 256 ? 1 : (d == 128 ? 2 : (lean_pass(d, mode, mfsum) ? 4 : 3));
+}
+
 template <int D, int BLK, int MODE, int ROWS, bool MFSUM>
-__global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 2)))
+__global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSUM))
     attn_bf16_kernel(AttnParams p) {
   using G = GeoB<D, BLK, MODE, ROWS>;
   static_assert(ROWS == 128 || MODE == kDense || MODE == kDenseMass, "256 rows: dense passes");
@@ -142,9 +170,10 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   int nblk = nb;
   const int* list = nullptr;
   if constexpr (MODE == kSparse) {
+    const int nbpad = ((nb + 63) / 64) * 64;  // as in GeoB::lds_bytes
     int* flag = (int*)(smem + G::kRingBytes);
-    int* lst = flag + G::kMaxBlocks;
-    int* ccount = lst + G::kMaxBlocks;
+    int* lst = flag + nbpad;
+    int* ccount = lst + nbpad;
     const int qb0 = w * G::kQPW;
     nblk = build_union_list<G::kQPW, G::kThreads, G::kMaxBlocks>(
         p.idx, p.cnt, (size_t)bh * nb + qb0, min(G::kQPW, nb - qb0), nb, flag, lst, ccount);
@@ -219,6 +248,10 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   // row in the B-operand layout of the P V product (lanes q and q + 32), so
   // register 0 of every lane accumulates its own row's full sum.
   constexpr bool kMfmaSum = MFSUM && (MODE == kDense || MODE == kSparse);
+  constexpr bool kLean = lean_pass(D, MODE, MFSUM);
+  // Lean passes with row sums on the matrix cores take the exponentials
+  // speculatively (see consume)
+  constexpr bool kSpecExp = kLean && kMfmaSum;
   f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
   bf16x8 rowsel;
   {
@@ -274,6 +307,25 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
         sc[0] = mfma_bf16(a0, qreg[dk], sc[0]);
         sc[1] = mfma_bf16(a1, qreg[dk], sc[1]);
       }
+    } else if constexpr (kLean) {
+      // the scores are on the step's critical path here: all eight K
+      // fragments are read before the first MFMA, so the LDS latency is paid
+      // once per tile rather than once per MFMA
+      bf16x8 af[2][D / 16];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int r = cc * 32 + prow;
+        const unsigned char* krow = slot + r * G::kRowBytes;
+#pragma unroll
+        for (int dk = 0; dk < D / 16; ++dk)
+          af[cc][dk] = *(const bf16x8*)(krow + swz_k<D>(r, 2 * dk + g) * 16);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[cc][i] = 0.f;
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int dk = 0; dk < D / 16; ++dk) sc[cc] = mfma_bf16(af[cc][dk], qreg[dk], sc[cc]);
     } else {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
@@ -316,26 +368,44 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   // probabilities, no raise, P V adds nothing, the same bits -- instead of
   // branching around it.  The union exceeds each list by ~3 %; measured
   // 0.7 % faster than the branch with the score MFMAs at a lower wave
-  // priority.  At D = 64 the softmax VALU is the bottleneck and the extra
-  // tiles made it 12 % slower.  The mass pass (no P V, every wave keeps
-  // every tile) and the D = 64 dense pass (128-row workgroups) issue them
+  // priority.  (At D = 64 the sparse pass runs lean instead, see
+  // lean_pass: issued inline there, the two score sets spill heavily at
+  // three waves per SIMD.)  The mass pass (no P V, every wave keeps every
+  // tile) and the D = 64 dense pass with lse (128-row workgroups) issue them
   // the same way: 1-2 % faster, the same bits.  (The 256-row dense passes
   // measured within noise, the D = 64 dense+mass pass 9 % slower.)
   constexpr bool kInline =
-      (MODE == kSparse && D == 128) || MODE == kMass || (MODE == kDense && D == 64);
+      (MODE == kSparse && D == 128) || MODE == kMass || (MODE == kDense && D == 64 && !kLean);
+
+  // keys past the sequence end score -inf (a final tile that runs past N)
+  auto mask_tail = [&](f32x16 (&sc)[2], int key0) {
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (key0 + cc * 32 + perm_row(c_row(i, g)) >= N) sc[cc][i] = -INFINITY;
+  };
+  // bf16 probabilities of tile t against the exponent reference m_e, packed
+  // in the B-operand layout of the P V product (slice h of chunk cc)
+  auto pack_probs = [&](const f32x16 (&sc)[2], float m_e, u32x4 (&pk)[2][2]) {
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          pk[cc][h][j] = pack_bf16x2(
+              __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][8 * h + 2 * j], c2, -m_e)),
+              __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][8 * h + 2 * j + 1], c2, -m_e)));
+  };
 
   // softmax of tile t (scores in sc) and its P V product; with kInline also
-  // the scores of the next tile (K in nslot) into sn.  keep is false for a
-  // tile this wave's query block did not keep (kInline only).
+  // the scores of the next tile (K in nslot) into sn, with kSpecExp nslot is
+  // the tile's own K (for a recompute).  keep is false for a tile this
+  // wave's query block did not keep (kInline only).
   auto consume = [&](int t, int key0, f32x16 (&sc)[2], auto masked,
                      const unsigned char* nslot, f32x16 (&sn)[2], bool keep) {
-    if constexpr (decltype(masked)::value) {
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (key0 + cc * 32 + perm_row(c_row(i, g)) >= N) sc[cc][i] = -INFINITY;
-    }
+    if constexpr (decltype(masked)::value) mask_tail(sc, key0);
     if constexpr (MODE == kMass) {
       compute_s(nslot, sn);
       float acc = 0.f;
@@ -346,6 +416,78 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
           acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc][i], c2, -lse_row));
       acc = wave_sum(acc);
       if (lane == 0) part[wave * G::kMaxBlocks + (key0 / BLK)] += acc;
+    } else if constexpr (kSpecExp) {
+      // Speculative exponentials: the probabilities are taken against the
+      // current reference first, and the row maxima only when they could
+      // matter.  A tile raises the reference of a row only if its scaled max
+      // exceeds the reference by more than kRaise = 16, and then that row's
+      // largest probability is above 2^16 (less rounding); so unless some
+      // bf16 probability of the wave exceeds 2^15 -- one maximum over the
+      // packed words -- no row raises, and the probabilities already taken
+      // are exactly those the exact path would take.  Otherwise (and on the
+      // wave's first kept tile, while the reference is -inf) the exact path
+      // runs: scores recomputed from the K tile (the speculative pass has
+      // consumed them), row maxima, raise and rescale, probabilities again.
+      // The outcome is the same bits as taking the maxima on every tile; the
+      // maxima (16 three-input maxes, a lane exchange and a compare per tile,
+      // ~15 % of the loop's VALU work) drop to 8 packed three-input maxes.
+      // bf16 bits of non-negative values order like the values, and so do
+      // they as f16 bits up to 0x7BFF; anything above (bf16 >= 2^121, inf)
+      // reads as f16 inf or NaN, which the maximum propagates and whose bits
+      // are also above the threshold.  Measured 1-1.5 % faster.
+      typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+      u32x4 pk[2][2];
+      pack_probs(sc, m_use, pk);
+      h2v hm = __builtin_bit_cast(h2v, pk[0][0][0]);
+#pragma unroll
+      for (int w = 1; w < 16; ++w)
+        hm = __builtin_elementwise_maximum(hm,
+                                           __builtin_bit_cast(h2v, pk[w >> 3][(w >> 2) & 1][w & 3]));
+      const unsigned mb = __builtin_bit_cast(unsigned, hm);
+      constexpr unsigned kSpecBits = 0x4700u;  // bf16 2^15
+      const bool over = (mb & 0xFFFFu) > kSpecBits || mb > ((kSpecBits << 16) | 0xFFFFu);
+      // (bitwise or: no branch between the score MFMAs and the exponentials)
+      const bool exact = (__ballot(m_thr == -INFINITY) != 0) | (__ballot(over) != 0);
+      if (exact) {
+        compute_s(nslot, sc);
+        if constexpr (decltype(masked)::value) mask_tail(sc, key0);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[cc][i]);
+        mx = pair_max(mx);
+        const float m_cand = mx * c2;
+        const bool raise = m_cand > m_thr;
+        if (__ballot(raise) != 0) {
+          float alpha = 1.0f;
+          if (raise) {
+            alpha = __builtin_amdgcn_exp2f(m_run - m_cand);
+            m_run = m_cand;
+            m_thr = m_run + kRaise;
+            m_use = (m_run == -INFINITY) ? 0.f : m_run;
+          }
+#pragma unroll
+          for (int mt = 0; mt < kORegs; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[mt][i] *= alpha;
+          lacc[0] *= alpha;
+        }
+        pack_probs(sc, m_use, pk);
+      }
+      const unsigned char* vs = vslot[t & 1];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[cc][h]);
+          lacc = mfma16_bf16(rowsel, pb, lacc);
+#pragma unroll
+          for (int mt = 0; mt < kORegs; ++mt) {
+            const bf16x8 a = v_operand(vs, cc * 32 + h * 16 + g * 8, mt);
+            oacc[mt] = mfma_bf16(a, pb, oacc[mt]);
+          }
+        }
     } else {
       // online softmax; the reference max is raised only when a probability
       // could exceed 2^kRaise, so O is rarely rescaled.  Everything that
@@ -500,6 +642,26 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
     }
     constexpr bool kHave = kWindow || kBatch;
     const int key0 = kHave ? key0_from(e0, t) : key0_of(t);
+    if constexpr (kLean) {
+      // K(t+1) and V(t+1) into the slots tile t-1 freed; then this tile's
+      // scores, softmax and P V.  The score MFMAs issue at the lowest wave
+      // priority, like the prefetched ones below (0.5-1 % faster than equal
+      // priorities here too)
+      if (t + 1 < ntile) {
+        const int k1 = kHave ? key0_from(e1, t + 1) : key0_of(t + 1);
+        dma_tile(kh, k1, kslot[(t + 1) & 1], koff);
+        dma_tile(vh, k1, vslot[(t + 1) & 1], voff);
+      }
+      if (MODE != kSparse || ((e0 >> (16 + qi)) & 1) != 0) {
+        __builtin_amdgcn_s_setprio(0);
+        compute_s(kslot[t & 1], sc);
+        __builtin_amdgcn_s_setprio(1);
+        consume(t, key0, sc, masked, kslot[t & 1], sn, true);
+      }
+      wait_dma_all();
+      __syncthreads();
+      return;
+    }
     flush_rowsum();
     // loads for later tiles: K(t+2) into the K slot freed by tile t, V(t+1)
     // into the V slot freed by tile t-1
@@ -546,7 +708,7 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
   if (ntile > 0) {
     dma_tile(kh, key0_of(0), kslot[0], koff);
     if constexpr (G::kWithV) dma_tile(vh, key0_of(0), vslot[0], voff);
-    if (ntile > 1) dma_tile(kh, key0_of(1), kslot[1], koff);
+    if (!kLean && ntile > 1) dma_tile(kh, key0_of(1), kslot[1], koff);
   }
   // Consume Q (and the row lse) here, on every path: the compiler then waits
   // for those loads once, before the loop, instead of placing vmcnt waits
@@ -559,8 +721,10 @@ __global__ void __launch_bounds__((ROWS * 2), (ROWS == 256 ? 1 : (D == 64 ? 3 : 
     __syncthreads();
     // (with kInline every wave runs the softmax of tile 0, so its scores
     // must be real numbers even where the wave's block did not keep it)
-    if (MODE != kSparse || kInline || member(0)) compute_s(kslot[0], sa);
-    __syncthreads();  // K slot 0 may be refilled from here on
+    if (!kLean) {
+      if (MODE != kSparse || kInline || member(0)) compute_s(kslot[0], sa);
+      __syncthreads();  // K slot 0 may be refilled from here on
+    }
   }
   const bool last_short = ntile > 0 && key0_of(ntile - 1) + 64 > N;
   if constexpr (kWindow) {
@@ -649,7 +813,7 @@ hipError_t launch_b(const AttnParams& p, hipStream_t stream) {
   const int wph = (p.nb + G::kQPW - 1) / G::kQPW;
   const int grid = p.order != nullptr ? (int)sparse_plan_slots((long long)wph * (p.items / p.nb))
                                        : xcd_grid(wph, p.items / p.nb);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(G::kThreads), G::kLdsBytes, stream, p);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(G::kThreads), G::lds_bytes(p.nb), stream, p);
   return hipGetLastError();
 }
 
