@@ -446,8 +446,9 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
       const unsigned mb = __builtin_bit_cast(unsigned, hm);
       constexpr unsigned kSpecBits = 0x4700u;  // bf16 2^15
       const bool over = (mb & 0xFFFFu) > kSpecBits || mb > ((kSpecBits << 16) | 0xFFFFu);
-      // (bitwise or: no branch between the score MFMAs and the exponentials)
-      const bool exact = (__ballot(m_thr == -INFINITY) != 0) | (__ballot(over) != 0);
+      // (one ballot of both lane conditions: no branch between the score
+      // MFMAs and the exponentials)
+      const bool exact = __ballot(m_thr == -INFINITY || over) != 0;
       if (exact) {
         compute_s(nslot, sc);
         if constexpr (decltype(masked)::value) mask_tail(sc, key0);
