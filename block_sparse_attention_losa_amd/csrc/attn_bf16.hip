@@ -595,9 +595,10 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
   // Each step reads the entry of tile t+3, a step before its first use, so
   // the loop never waits on an LDS read of the list (reading entries t, t+1,
   // t+2 where they are used costs one LDS round trip each, per step):
-  // measured 1.2 % faster.  At D = 64 the three carried registers add spills
-  // in the three-waves-per-SIMD budget (2 % slower), so that kernel reads the
-  // step's three entries together at its start instead: one wait per step.
+  // measured 1.2 % faster.  At D = 64 the three carried registers spilled
+  // (measured with the score prefetch at three waves per SIMD: 2 % slower),
+  // so that kernel reads the step's entries together at its start instead,
+  // one wait per step (the lean step uses those of tiles t and t+1).
   constexpr bool kWindow = MODE == kSparse && D == 128;
   constexpr bool kBatch = MODE == kSparse && !kWindow;
   int win0 = 0, win1 = 0, win2 = 0;
@@ -611,8 +612,8 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
     return (e & 0xFFFF) * BLK + (G::kSubs == 1 ? 0 : (t & 1) * 64);
   };
 
-  // Wave priorities (below) pay off when the two waves sharing a SIMD come
-  // from different workgroups, whose steps drift apart; in a 256-row
+  // Wave priorities (below) pay off when the waves sharing a SIMD come from
+  // different workgroups, whose steps drift apart; in a 256-row
   // workgroup (one per CU) both are in the same workgroup, in lockstep, and
   // equal priorities are 1.3 % faster there.  With kInline the score MFMAs
   // share the softmax block, so there is no separate phase to rank.
