@@ -31,6 +31,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_wan13_traffic.json")
 SELECT_COUNTERS_FILE = os.path.join(ROOT, "profiles", "select_kernel_counters.json")
+CLOCK_FILE = os.path.join(ROOT, "profiles", "sustained_clock.json")
 CSRC = os.path.join(ROOT, "block_sparse_attention_losa_amd", "csrc")
 KERNEL_SOURCES = [os.path.join(CSRC, f)
                   for f in ("attn_bf16.hip", "attn_common.h", "losa_device.h",
@@ -91,6 +92,27 @@ def read_traffic(n_launch_units):
     if rec.get("kernel_sha") != kernel_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+def read_sustained_clock(workload, achieved_tflops):
+    """The shader clock the timed sparse kernel sustains on this workload
+    (rocprofv3: GRBM_GUI_ACTIVE per XCD over the dispatch time, mean over
+    boxes), and the achieved rate against the MFMA peak at that clock.  None
+    when absent, for another workload, or taken on another kernel source."""
+    if not os.path.exists(CLOCK_FILE):
+        return None
+    with open(CLOCK_FILE) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_sha") != kernel_hash():
+        return None
+    entry = rec.get("workloads", {}).get(workload)
+    if not entry:
+        return None
+    ghz = float(entry["ghz"])
+    peak = PEAK_BF16_TFLOPS * ghz / CLOCK_GHZ
+    return {"ghz": ghz, "peak_at_clock": round(peak, 1),
+            "frac_at_clock": round(achieved_tflops / peak, 4),
+            "source": "profiles/sustained_clock.json"}
 
 
 def select_floor_ms(rows, nkb):
@@ -435,6 +457,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
+        "sustained_clock": read_sustained_clock(cfg.name, achieved),
         "kept_fraction": round(f, 4),
         "mfma_util": round(achieved / PEAK_BF16_TFLOPS, 4),
         "x_vs_dense": round(dense_mean / sparse_mean, 3) if dense_mean else None,

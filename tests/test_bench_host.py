@@ -63,3 +63,20 @@ def test_select_floor_from_counted_instructions():
     assert bench.select_floor_ms(100, 929) == 100 * rec["valu_instructions_per_row"]["1024"] \
         * 4 / 1024 / 2.4e9 * 1e3
     assert bench.select_floor_ms(100, 100) is None                  # size 128 not counted
+
+
+def test_sustained_clock_is_tied_to_the_kernel_source(tmp_path, monkeypatch):
+    import json
+    rec = {"kernel_sha": bench.kernel_hash(), "nominal_ghz": 2.4,
+           "workloads": {"w": {"ghz": 1.8, "boxes": []}}}
+    path = tmp_path / "clock.json"
+    path.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "CLOCK_FILE", str(path))
+    got = bench.read_sustained_clock("w", 1125.0)
+    # peak at 1.8 GHz = 2500 * 1.8 / 2.4 = 1875 TFLOP/s
+    assert got["ghz"] == 1.8 and got["peak_at_clock"] == 1875.0
+    assert got["frac_at_clock"] == 0.6
+    assert bench.read_sustained_clock("other", 1125.0) is None
+    rec["kernel_sha"] = "0" * 16
+    path.write_text(json.dumps(rec))
+    assert bench.read_sustained_clock("w", 1125.0) is None
