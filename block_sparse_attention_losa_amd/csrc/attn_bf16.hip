@@ -42,11 +42,12 @@
 //    ahead of it at a lower wave priority, so the two waves of a SIMD (from
 //    different workgroups) tend to alternate between the matrix core and
 //    the VALU;
-//  * except at D = 64 without lse and for D = 64 sparse attention ("lean"
-//    passes): there K and V both run one tile ahead, a tile's scores are
-//    computed in its own step, and the 32 registers this saves give four
-//    waves per SIMD instead of three; the lean passes without lse also take
-//    the exponentials speculatively, before the row maxima.
+//  * except in the D = 64 passes with a P V product other than dense
+//    attention with lse ("lean" passes): there K and V both run one tile
+//    ahead, a tile's scores are computed in its own step, and the 32
+//    registers this saves give four waves per SIMD instead of three; the
+//    lean passes without lse also take the exponentials speculatively,
+//    before the row maxima.
 //
 // Scores are computed transposed, S^T = K Q^T, on 32x32x16 MFMA tiles: a
 // lane then holds one query row and 16 of the 32 keys of a chunk, so row
@@ -87,18 +88,20 @@ struct GeoB {
   }
 };
 
-// The D = 64 passes with a P V product and no lse -- sparse attention (with
-// or without lse) and dense attention without lse -- run "lean": the scores
+// The D = 64 passes with a P V product -- sparse attention (with or without
+// lse), dense attention without lse and the one-sweep construction -- run
+// "lean": the scores
 // of a tile are computed at the start of its own step instead of one step
 // ahead, which frees the 32 registers of the second score set, and the loop
 // fits 128 VGPRs: four waves per SIMD.  At D = 64 a score carries half the
 // matrix work of D = 128 and the same softmax work, so the loop is bound by
 // latency and VALU issue rather than the matrix cores, and the fourth wave
 // hides more of it than the overlap the score prefetch gave within a wave
-// (sparse, CogVideoX layer: 4-5 % faster than three waves with prefetch; the
-// dense lse pass keeps the prefetch, which spills at 128 VGPRs).
+// (sparse, CogVideoX layer: 4-5 % faster than three waves with prefetch;
+// one-sweep construction 4 % faster; the dense pass with lse keeps the
+// prefetch, which spilled in its loop at 128 VGPRs).
 constexpr bool lean_pass(int d, int mode, bool mfsum) {
-  return d == 64 && (mode == kSparse || (mode == kDense && mfsum));
+  return d == 64 && (mode == kSparse || (mode == kDense && mfsum) || mode == kDenseMass);
 }
 
 // Workgroups per CU the register budget is sized for.  Two waves per SIMD at
@@ -645,6 +648,7 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
     constexpr bool kHave = kWindow || kBatch;
     const int key0 = kHave ? key0_from(e0, t) : key0_of(t);
     if constexpr (kLean) {
+      flush_rowsum();
       // K(t+1) and V(t+1) into the slots tile t-1 freed; then this tile's
       // scores, softmax and P V.  The score MFMAs issue at the lowest wave
       // priority, like the prefetched ones below (0.5-1 % faster than equal
