@@ -129,13 +129,15 @@ def _cmp(o, lse, o_ref, lse_ref, what):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("blk", [64, 128])
 @pytest.mark.parametrize("d", [64, 128])
-def test_reference_raises_match_oracle(losa, d):
-    n = 64 * 8 + 17  # nine tiles, the last one ragged
-    blk = 64
+def test_reference_raises_match_oracle(losa, d, blk):
+    # nine 64-key tiles, the last one ragged; with 128-token blocks the last
+    # block's second tile is empty
+    n = 64 * 8 + 17
     nb = (n + blk - 1) // blk
     q, k, v = _inputs(d, n, seed=700 + d)
-    _say(f"[raise] D{d} N{n}: dense")
+    _say(f"[raise] D{d} block {blk} N{n}: dense")
     tq, tk, tv = (torch.from_numpy(x).cuda().to(torch.bfloat16) for x in (q, k, v))
     o, lse = losa.dense_attn(tq, tk, tv, block=blk)
     on, _ = losa.dense_attn(tq, tk, tv, block=blk, want_lse=False)
@@ -145,7 +147,7 @@ def test_reference_raises_match_oracle(losa, d):
     _say(f"[raise] D{d}: sparse over every block")
     so, sl = losa.sparse_attn(tq, tk, tv, fi, fc, block=blk, want_lse=True)
     sn, _ = losa.sparse_attn(tq, tk, tv, fi, fc, block=blk)
-    rng = np.random.default_rng(900 + d)
+    rng = np.random.default_rng(900 + d + blk)
     idx, cnt = _random_lists(nb, 4, rng)
     ti, tc = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
     plan = losa.sparse_plan(tc, block=blk, head_dim=d)
@@ -161,11 +163,11 @@ def test_reference_raises_match_oracle(losa, d):
          (("o", o), ("lse", lse), ("on", on), ("ro", ro), ("rl", rl), ("rn", rn))}
     for h in range(4):
         od, ld = oracle.dense_attention(q[0, h], k[0, h], v[0, h])
-        _cmp(g["o"][0, h], g["lse"][0, h], od, ld, f"D{d} h{h} dense")
-        _cmp(g["on"][0, h], None, od, None, f"D{d} h{h} dense no-lse")
+        _cmp(g["o"][0, h], g["lse"][0, h], od, ld, f"D{d} b{blk} h{h} dense")
+        _cmp(g["on"][0, h], None, od, None, f"D{d} b{blk} h{h} dense no-lse")
         os_, ls_ = oracle.sparse_attention(q[0, h], k[0, h], v[0, h], idx[0, h], cnt[0, h], blk)
-        _cmp(g["ro"][0, h], g["rl"][0, h], os_, ls_, f"D{d} h{h} sparse")
-        _cmp(g["rn"][0, h], None, os_, None, f"D{d} h{h} sparse no-lse")
+        _cmp(g["ro"][0, h], g["rl"][0, h], os_, ls_, f"D{d} b{blk} h{h} sparse")
+        _cmp(g["rn"][0, h], None, os_, None, f"D{d} b{blk} h{h} sparse no-lse")
 
 
 @pytest.mark.gpu
