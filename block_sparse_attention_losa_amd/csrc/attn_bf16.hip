@@ -46,8 +46,9 @@
 //    attention with lse ("lean" passes): there K and V both run one tile
 //    ahead, a tile's scores are computed in its own step, and the 32
 //    registers this saves give four waves per SIMD instead of three; the
-//    lean passes without lse also take the exponentials speculatively,
-//    before the row maxima.
+//    lean passes without lse take row maxima only on a wave's first kept
+//    tile and keep that reference, with a second walk over the tiles for a
+//    workgroup whose sums leave the fp32 range.
 //
 // Scores are computed transposed, S^T = K Q^T, on 32x32x16 MFMA tiles: a
 // lane then holds one query row and 16 of the 32 keys of a chunk, so row
@@ -80,11 +81,13 @@ struct GeoB {
   static constexpr int kRingBytes = (kWithV ? 4 : 2) * kTileBytes;  // 2 K + 2 V tiles
   static constexpr int kAuxBytes =
       MODE == kSparse ? (2 * kMaxBlocks + 16) * 4 : (MODE == kMass ? 4 * kMaxBlocks * 4 : 0);
-  static constexpr int kLdsBytes = kRingBytes + kAuxBytes;
+  // the last 16 bytes hold the word that sends a workgroup through its
+  // tiles a second time (see the tile loop)
+  static constexpr int kLdsBytes = kRingBytes + kAuxBytes + 16;
   // sparse: the union list's flags and entries take one slot per key block
   // (rounded up to 64), so a short sequence leaves LDS for more workgroups
   static constexpr int lds_bytes(int nb) {
-    return MODE == kSparse ? kRingBytes + (2 * ((nb + 63) / 64) * 64 + 16) * 4 : kLdsBytes;
+    return MODE == kSparse ? kRingBytes + (2 * ((nb + 63) / 64) * 64 + 16) * 4 + 16 : kLdsBytes;
   }
 };
 
@@ -252,9 +255,11 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
   // register 0 of every lane accumulates its own row's full sum.
   constexpr bool kMfmaSum = MFSUM && (MODE == kDense || MODE == kSparse);
   constexpr bool kLean = lean_pass(D, MODE, MFSUM);
-  // Lean passes with row sums on the matrix cores take the exponentials
-  // speculatively (see consume)
+  // Lean passes with row sums on the matrix cores keep the reference of a
+  // wave's first kept tile (see consume)
   constexpr bool kSpecExp = kLean && kMfmaSum;
+  bool spec_first = true;  // kSpecExp: the wave has not yet taken a tile's row maxima
+  bool redo = false;       // kSpecExp: second walk over the tiles, exact path on every tile
   f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
   bf16x8 rowsel;
   {
@@ -420,41 +425,21 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
       acc = wave_sum(acc);
       if (lane == 0) part[wave * G::kMaxBlocks + (key0 / BLK)] += acc;
     } else if constexpr (kSpecExp) {
-      // Speculative exponentials: the probabilities are taken against the
-      // current reference first, and the row maxima only when they could
-      // matter.  A tile raises the reference of a row only if its scaled max
-      // exceeds the reference by more than kRaise = 16, and then that row's
-      // largest probability is above 2^16 (less rounding); so unless some
-      // bf16 probability of the wave exceeds 2^15 -- one maximum over the
-      // packed words -- no row raises, and the probabilities already taken
-      // are exactly those the exact path would take.  Otherwise (and on the
-      // wave's first kept tile, while the reference is -inf) the exact path
-      // runs: scores recomputed from the K tile (the speculative pass has
-      // consumed them), row maxima, raise and rescale, probabilities again.
-      // The outcome is the same bits as taking the maxima on every tile; the
-      // maxima (16 three-input maxes, a lane exchange and a compare per tile,
-      // ~15 % of the loop's VALU work) drop to 8 packed three-input maxes.
-      // bf16 bits of non-negative values order like the values, and so do
-      // they as f16 bits up to 0x7BFF; anything above (bf16 >= 2^121, inf)
-      // reads as f16 inf or NaN, which the maximum propagates and whose bits
-      // are also above the threshold.  Measured 1-1.5 % faster.
-      typedef _Float16 h2v __attribute__((ext_vector_type(2)));
-      u32x4 pk[2][2];
-      pack_probs(sc, m_use, pk);
-      h2v hm = __builtin_bit_cast(h2v, pk[0][0][0]);
-#pragma unroll
-      for (int w = 1; w < 16; ++w)
-        hm = __builtin_elementwise_maximum(hm,
-                                           __builtin_bit_cast(h2v, pk[w >> 3][(w >> 2) & 1][w & 3]));
-      const unsigned mb = __builtin_bit_cast(unsigned, hm);
-      constexpr unsigned kSpecBits = 0x4700u;  // bf16 2^15
-      const bool over = (mb & 0xFFFFu) > kSpecBits || mb > ((kSpecBits << 16) | 0xFFFFu);
-      // (one ballot of both lane conditions: no branch between the score
-      // MFMAs and the exponentials)
-      const bool exact = __ballot(m_thr == -INFINITY || over) != 0;
-      if (exact) {
-        compute_s(nslot, sc);
-        if constexpr (decltype(masked)::value) mask_tail(sc, key0);
+      // No row maxima after a wave's first kept tile: the probabilities are
+      // taken against the reference that tile set, whatever the later
+      // scores.  Their bf16 values and the fp32 sums and products keep
+      // their relative precision at any size fp32 holds, so the result
+      // differs from one taken with a raised reference only in rounding;
+      // a row whose later logits exceed its first tile's maximum by more
+      // than ~88 (natural units) overflows to inf or NaN, which the check
+      // after the tile loop sees, and the workgroup then walks its tiles
+      // once more with the lazy rule of the exact path (raise past 2^16)
+      // on every tile.  The first kept tile, while the reference is -inf,
+      // and every tile of that second walk take the exact path: row
+      // maxima, raise and rescale.  Against a test for large probabilities
+      // on every tile (packed maxima over the 16 words and a ballot) this
+      // drops ~15 VALU instructions per tile.
+      if (spec_first || redo) {
         float mx = -INFINITY;
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
@@ -477,8 +462,10 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
             for (int i = 0; i < 16; ++i) oacc[mt][i] *= alpha;
           lacc[0] *= alpha;
         }
-        pack_probs(sc, m_use, pk);
+        spec_first = false;
       }
+      u32x4 pk[2][2];
+      pack_probs(sc, m_use, pk);
       const unsigned char* vs = vslot[t & 1];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
@@ -711,48 +698,83 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
   using Plain = std::integral_constant<bool, false>;
   using Masked = std::integral_constant<bool, true>;
   f32x16 sa[2], sb[2];
-  if (ntile > 0) {
-    dma_tile(kh, key0_of(0), kslot[0], koff);
-    if constexpr (G::kWithV) dma_tile(vh, key0_of(0), vslot[0], voff);
-    if (!kLean && ntile > 1) dma_tile(kh, key0_of(1), kslot[1], koff);
-  }
-  // Consume Q (and the row lse) here, on every path: the compiler then waits
-  // for those loads once, before the loop, instead of placing vmcnt waits
-  // inside the loop where they would also stall on the tile loads in flight.
-#pragma unroll
-  for (int dk = 0; dk < D / 16; ++dk) asm volatile("" ::"v"(qreg[dk]));
-  asm volatile("" ::"v"(lse_row));
-  if (ntile > 0) {
-    wait_dma_all();
-    __syncthreads();
-    // (with kInline every wave runs the softmax of tile 0, so its scores
-    // must be real numbers even where the wave's block did not keep it)
-    if (!kLean) {
-      if (MODE != kSparse || kInline || member(0)) compute_s(kslot[0], sa);
-      __syncthreads();  // K slot 0 may be refilled from here on
+  int* redo_word = (int*)(smem + G::lds_bytes(nb) - 16);
+  if constexpr (kSpecExp)
+    if (tid == 0) *redo_word = 0;  // ordered before any use by the barriers below
+  for (;;) {
+    if (ntile > 0) {
+      dma_tile(kh, key0_of(0), kslot[0], koff);
+      if constexpr (G::kWithV) dma_tile(vh, key0_of(0), vslot[0], voff);
+      if (!kLean && ntile > 1) dma_tile(kh, key0_of(1), kslot[1], koff);
     }
-  }
-  const bool last_short = ntile > 0 && key0_of(ntile - 1) + 64 > N;
-  if constexpr (kWindow) {
-    win0 = ntile > 0 ? raw_entry(0) : 0;
-    win1 = ntile > 1 ? raw_entry(1) : 0;
-    win2 = ntile > 2 ? raw_entry(2) : 0;
-  }
-  const int nplain = ntile - (last_short ? 1 : 0);
-  int t = 0;
-  for (; t + 1 < nplain; t += 2) {
-    step(t, sa, sb, Plain());
-    step(t + 1, sb, sa, Plain());
-  }
-  if (t < nplain) {
-    step(t, sa, sb, Plain());
-    ++t;
-  }
-  if (last_short) {
-    if (t & 1)
-      step(t, sb, sa, Masked());
-    else
-      step(t, sa, sb, Masked());
+    // Consume Q (and the row lse) here, on every path: the compiler then waits
+    // for those loads once, before the loop, instead of placing vmcnt waits
+    // inside the loop where they would also stall on the tile loads in flight.
+#pragma unroll
+    for (int dk = 0; dk < D / 16; ++dk) asm volatile("" ::"v"(qreg[dk]));
+    asm volatile("" ::"v"(lse_row));
+    if (ntile > 0) {
+      wait_dma_all();
+      __syncthreads();
+      // (with kInline every wave runs the softmax of tile 0, so its scores
+      // must be real numbers even where the wave's block did not keep it)
+      if (!kLean) {
+        if (MODE != kSparse || kInline || member(0)) compute_s(kslot[0], sa);
+        __syncthreads();  // K slot 0 may be refilled from here on
+      }
+    }
+    const bool last_short = ntile > 0 && key0_of(ntile - 1) + 64 > N;
+    if constexpr (kWindow) {
+      win0 = ntile > 0 ? raw_entry(0) : 0;
+      win1 = ntile > 1 ? raw_entry(1) : 0;
+      win2 = ntile > 2 ? raw_entry(2) : 0;
+    }
+    const int nplain = ntile - (last_short ? 1 : 0);
+    int t = 0;
+    for (; t + 1 < nplain; t += 2) {
+      step(t, sa, sb, Plain());
+      step(t + 1, sb, sa, Plain());
+    }
+    if (t < nplain) {
+      step(t, sa, sb, Plain());
+      ++t;
+    }
+    if (last_short) {
+      if (t & 1)
+        step(t, sb, sa, Masked());
+      else
+        step(t, sa, sb, Masked());
+    }
+
+    // kSpecExp: a row sum or output that left the fp32 range (a logit far
+    // above the row's first kept tile; see consume) sends the whole
+    // workgroup -- the tile loads are shared -- through its tiles again on
+    // the exact path.  Finite values pass; inf and NaN do not.
+    if constexpr (kSpecExp) {
+      if (!redo && ntile > 0) {
+        float tot = lacc[0];
+#pragma unroll
+        for (int mt = 0; mt < kORegs; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) tot += fabsf(oacc[mt][i]);
+        if (__ballot(!(tot <= 3.0e38f)) != 0 && lane == 0) *redo_word = 1;
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(*redo_word) != 0) {
+          redo = true;
+          spec_first = true;
+#pragma unroll
+          for (int mt = 0; mt < kORegs; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[mt][i] = 0.f;
+          lacc = f32x4{0.f, 0.f, 0.f, 0.f};
+          m_run = -INFINITY;
+          m_thr = -INFINITY;
+          m_use = 0.f;
+          continue;
+        }
+      }
+    }
+    break;
   }
 
   // ------------------------------------------------------------ epilogue

@@ -1,16 +1,18 @@
 """GPU parity on inputs built to move the softmax reference.
 
 The kernels take probabilities against a per-row reference that is raised
-only when a tile's scaled maximum exceeds it by more than 16 (log2 units),
-and the D = 64 passes without lse take them speculatively, computing the
-row maxima only when some probability exceeds 2^15.  Random inputs rarely
+only when a tile's scaled maximum exceeds it by more than 16 (log2 units);
+the D = 64 passes without lse take row maxima only on a wave's first kept
+tile and keep that reference unless a row sum or output leaves the fp32
+range, which sends the workgroup through its tiles again with the raise
+rule on every tile.  Random inputs rarely
 raise the reference after a row's first tile, so these inputs set the score
 level of every 64-key tile explicitly (one coordinate of q is 1, the same
 coordinate of k carries the level; the other coordinates are small noise):
 
   * head 0: +20 per tile, a raise on every tile;
-  * head 1: +15.5 per tile, over the speculative test's 2^15 on every tile
-    but over the raise threshold only every other tile;
+  * head 1: +15.5 per tile, within one of the raise threshold on every tile
+    but over it only every other tile;
   * head 2: a zigzag (+45, -25, ...), raises on the rises only;
   * head 3: random tile levels in [0, 60].
 
@@ -181,3 +183,85 @@ def test_reference_raises_fp32(losa):
     for h in range(4):
         od, ld = oracle.dense_attention(q[0, h], k[0, h], v[0, h])
         _cmp(o[0, h].cpu().numpy(), lse[0, h].cpu().numpy(), od, ld, f"fp32 h{h} dense")
+
+
+def _jump_inputs(d, n, seed):
+    """Eight heads; in head o every query row scores ~0 against every key
+    except two: key 64 + 8m + o (tile 1) scores +100 and key 192 + 8m' + o
+    (tile 3) +110 (natural units; m, m' drawn per head), so each row's
+    maximum jumps twice, far past the raise threshold, and always at key
+    offset o within the eight consecutive keys a lane holds.  Taken against
+    the first tile's reference those probabilities would be 2^144 and
+    2^159, beyond fp32: only a raise keeps them finite."""
+    rng = np.random.default_rng(seed)
+    heads = 8
+    c = 1.0 / math.sqrt(d)
+    q = rng.normal(0.0, 0.05, (1, heads, n, d))
+    k = rng.normal(0.0, 0.05, (1, heads, n, d))
+    v = rng.normal(0.0, 1.0, (1, heads, n, d))
+    q[..., 0] = 1.0
+    k[..., 0] = 0.0
+    jumps = []
+    for o in range(heads):
+        j1 = 64 + 8 * int(rng.integers(0, 8)) + o
+        j2 = 192 + 8 * int(rng.integers(0, 8)) + o
+        k[0, o, j1, 0] = 100.0 / c
+        k[0, o, j2, 0] = 110.0 / c
+        jumps.append((j1, j2))
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).float().numpy() for x in (q, k, v))
+    return q, k, v, jumps
+
+
+def test_jump_inputs_place_the_maxima():
+    """Not a GPU check: the row maxima of head o sit at key offset o."""
+    n, d = 64 * 6 + 17, 64
+    q, k, _, jumps = _jump_inputs(d, n, seed=41)
+    for o, (j1, j2) in enumerate(jumps):
+        s = q[0, o].astype(np.float64) @ k[0, o].astype(np.float64).T / math.sqrt(d)
+        assert j1 % 8 == o and j2 % 8 == o and j1 // 64 == 1 and j2 // 64 == 3
+        assert np.all(np.argmax(s, axis=1) == j2)
+        assert np.all(s[:, j1] > 99.0) and np.all(s[:, j2] > 109.0)
+        assert np.all(np.delete(s, [j1, j2], axis=1) < 1.0)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("blk", [64, 128])
+@pytest.mark.parametrize("d", [64, 128])
+def test_jump_at_every_key_offset(losa, d, blk):
+    """A jump far above a row's first tile, at every key offset within a
+    lane's eight keys: the D = 64 passes without lse overflow on it and
+    must take their second, exact walk over the tiles (an earlier form of
+    those passes tested the probabilities of keys 0 and 1 of each group of
+    eight only, and the others then overflowed into the output)."""
+    n = 64 * 6 + 17
+    nb = (n + blk - 1) // blk
+    q, k, v, _ = _jump_inputs(d, n, seed=4100 + d + blk)
+    tq, tk, tv = (torch.from_numpy(x).cuda().to(torch.bfloat16) for x in (q, k, v))
+    _say(f"[jump] D{d} block {blk} N{n}: dense, sparse")
+    o, lse = losa.dense_attn(tq, tk, tv, block=blk)
+    on, _ = losa.dense_attn(tq, tk, tv, block=blk, want_lse=False)
+    rng = np.random.default_rng(4200 + d + blk)
+    idx, cnt = _random_lists(nb, 8, rng)
+    # every list keeps the blocks of both jumps (and tile 0's block, so the
+    # first kept tile is not the jump's)
+    must = sorted({0, 64 // blk, 192 // blk})
+    for h in range(8):
+        for i in range(nb):
+            keep = sorted(set(idx[0, h, i, :cnt[0, h, i]].tolist()) | set(must))
+            idx[0, h, i, :len(keep)] = keep
+            cnt[0, h, i] = len(keep)
+    ti, tc = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    rn, _ = losa.sparse_attn(tq, tk, tv, ti, tc, block=blk)
+    ro, rl = losa.sparse_attn(tq, tk, tv, ti, tc, block=blk, want_lse=True)
+    torch.cuda.synchronize()
+    g = {name: t.float().cpu().numpy() for name, t in
+         (("o", o), ("lse", lse), ("on", on), ("rn", rn), ("ro", ro), ("rl", rl))}
+    for name in g:
+        assert np.isfinite(g[name]).all(), (d, blk, name)
+    for h in range(8):
+        od, ld = oracle.dense_attention(q[0, h], k[0, h], v[0, h])
+        _cmp(g["o"][0, h], g["lse"][0, h], od, ld, f"D{d} b{blk} h{h} dense")
+        _cmp(g["on"][0, h], None, od, None, f"D{d} b{blk} h{h} dense no-lse")
+        os_, ls_ = oracle.sparse_attention(q[0, h], k[0, h], v[0, h], idx[0, h], cnt[0, h], blk)
+        _cmp(g["rn"][0, h], None, os_, None, f"D{d} b{blk} h{h} sparse no-lse")
+        _cmp(g["ro"][0, h], g["rl"][0, h], os_, ls_, f"D{d} b{blk} h{h} sparse")
