@@ -13,7 +13,7 @@
 //
 // One workgroup (4 waves) owns 128 query rows -- two 64-row query blocks or
 // one 128-row block -- and each wave owns 32 of them; the dense passes at
-// D = 128 use 256-row workgroups of 8 waves (one per CU).  Every 64-key K/V
+// D = 128 that write lse use 256-row workgroups of 8 waves (one per CU).  Every 64-key K/V
 // tile brought into LDS therefore feeds 128 (or 256) rows, which halves (or
 // quarters) the L2 traffic per flop compared with one 64-row block per
 // workgroup; at 64 rows the K/V feed alone would need the whole L2
@@ -35,20 +35,21 @@
 //    dim) are free of bank conflicts;
 //  * K runs one tile ahead of V: the scores of tile t+1 are computed on the
 //    matrix cores while tile t's softmax runs on the VALU, and the loads of
-//    K(t+2) and V(t+1) are in flight during both.  The D = 128 sparse pass,
-//    the mass pass and the D = 64 dense pass issue those score MFMAs inside
-//    the softmax block,
-//    interleaved with the exponentials; the other 128-row passes issue them
-//    ahead of it at a lower wave priority, so the two waves of a SIMD (from
-//    different workgroups) tend to alternate between the matrix core and
-//    the VALU;
-//  * except in the D = 64 passes with a P V product other than dense
-//    attention with lse ("lean" passes): there K and V both run one tile
-//    ahead, a tile's scores are computed in its own step, and the 32
-//    registers this saves give four waves per SIMD instead of three; the
-//    lean passes without lse take row maxima only on a wave's first kept
-//    tile and keep that reference, with a second walk over the tiles for a
-//    workgroup whose sums leave the fp32 range.
+//    K(t+2) and V(t+1) are in flight during both.  The D = 128 sparse pass
+//    with lse, the mass pass and the D = 64 dense pass with lse issue those
+//    score MFMAs inside the softmax block, interleaved with the
+//    exponentials; the other prefetching 128-row passes issue them ahead of
+//    it at a lower wave priority, so the two waves of a SIMD (from different
+//    workgroups) tend to alternate between the matrix core and the VALU;
+//  * except in the "lean" passes (lean_pass: at D = 64 every pass with a
+//    P V product but dense attention with lse, at D = 128 sparse and dense
+//    attention without lse): there K and V both run one tile ahead, a tile's
+//    scores are computed in its own step, a wave skips the tiles its block
+//    did not keep, and at D = 64 the 32 registers this saves give four
+//    waves per SIMD instead of three; the lean passes without lse take row
+//    maxima only on a wave's first kept tile and keep that reference, with
+//    a second walk over the tiles for a workgroup whose sums leave the fp32
+//    range.
 //
 // Scores are computed transposed, S^T = K Q^T, on 32x32x16 MFMA tiles: a
 // lane then holds one query row and 16 of the 32 keys of a chunk, so row
@@ -91,20 +92,28 @@ struct GeoB {
   }
 };
 
-// The D = 64 passes with a P V product -- sparse attention (with or without
-// lse), dense attention without lse and the one-sweep construction -- run
-// "lean": the scores
-// of a tile are computed at the start of its own step instead of one step
-// ahead, which frees the 32 registers of the second score set, and the loop
-// fits 128 VGPRs: four waves per SIMD.  At D = 64 a score carries half the
-// matrix work of D = 128 and the same softmax work, so the loop is bound by
-// latency and VALU issue rather than the matrix cores, and the fourth wave
-// hides more of it than the overlap the score prefetch gave within a wave
-// (sparse, CogVideoX layer: 4-5 % faster than three waves with prefetch;
-// one-sweep construction 4 % faster; the dense pass with lse keeps the
-// prefetch, which spilled in its loop at 128 VGPRs).
+// "Lean" passes compute a tile's scores at the start of its own step instead
+// of one step ahead, and a wave skips outright the tiles its query block did
+// not keep.  At D = 64 -- sparse attention (with or without lse), dense
+// attention without lse and the one-sweep construction -- this frees the 32
+// registers of the second score set and the loop fits 128 VGPRs: four waves
+// per SIMD.  A score there carries half the matrix work of D = 128 and the
+// same softmax work, so the loop is bound by latency and VALU issue rather
+// than the matrix cores, and the fourth wave hides more of it than the
+// overlap the score prefetch gave within a wave (sparse, CogVideoX layer:
+// 4-5 % faster than three waves with prefetch; one-sweep construction 4 %
+// faster; the dense pass with lse keeps the prefetch, which spilled in its
+// loop at 128 VGPRs).  At D = 128 the passes without lse (sparse and dense,
+// 128-row workgroups) run lean as well, still two waves per SIMD: the
+// sparse pass then does no work on the ~3 % of its workgroup's union tiles
+// its own query block did not keep, and with the first-tile reference (see
+// consume) no per-tile row maxima; measured 3.6-3.7 % faster on the
+// Wan2.1-1.3B and HunyuanVideo layers than the prefetching form, and the
+// 128-row lean dense pass within 0.3 % of the 256-row prefetching one, so
+// sparse attention over every block stays bit-identical to it.
 constexpr bool lean_pass(int d, int mode, bool mfsum) {
-  return d == 64 && (mode == kSparse || (mode == kDense && mfsum) || mode == kDenseMass);
+  return (d == 64 && (mode == kSparse || (mode == kDense && mfsum) || mode == kDenseMass)) ||
+         (d == 128 && (mode == kSparse || mode == kDense) && mfsum);
 }
 
 // Workgroups per CU the register budget is sized for.  Two waves per SIMD at
@@ -368,17 +377,17 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
     return __builtin_bit_cast(bf16x8, wv);
   };
 
-  // Sparse at D = 128: the next tile's score MFMAs are issued inside the
-  // softmax block (after the rare raise branch), where the scheduler
+  // Sparse at D = 128 with lse: the next tile's score MFMAs are issued inside
+  // the softmax block (after the rare raise branch), where the scheduler
   // interleaves them with the exponentials.  That needs the softmax on every
   // tile of the union, so a wave whose query block did not keep the tile
   // runs it against an exponent reference of +inf -- exact zero
   // probabilities, no raise, P V adds nothing, the same bits -- instead of
   // branching around it.  The union exceeds each list by ~3 %; measured
   // 0.7 % faster than the branch with the score MFMAs at a lower wave
-  // priority.  (At D = 64 the sparse pass runs lean instead, see
-  // lean_pass: issued inline there, the two score sets spill heavily at
-  // three waves per SIMD.)  The mass pass (no P V, every wave keeps every
+  // priority.  (The sparse passes at D = 64, and at D = 128 without lse,
+  // run lean instead, see lean_pass; at D = 64 issued inline, the two score
+  // sets spill heavily at three waves per SIMD.)  The mass pass (no P V, every wave keeps every
   // tile) and the D = 64 dense pass with lse (128-row workgroups) issue them
   // the same way: 1-2 % faster, the same bits.  (The 256-row dense passes
   // measured within noise, the D = 64 dense+mass pass 9 % slower.)
@@ -851,7 +860,7 @@ hipError_t launch_b_mode(int mode, const AttnParams& p, hipStream_t stream) {
     // without an lse output the row sums go to the matrix cores
     case kDense:
       return p.lse == nullptr
-                 ? launch_b<D, BLK, kDense, attn_rows(kDense, D, BLK), true>(p, stream)
+                 ? launch_b<D, BLK, kDense, attn_rows(kDense, D, BLK, false), true>(p, stream)
                  : launch_b<D, BLK, kDense, attn_rows(kDense, D, BLK)>(p, stream);
     case kSparse:
       return p.lse == nullptr

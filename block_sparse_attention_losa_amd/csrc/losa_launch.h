@@ -66,14 +66,19 @@ hipError_t launch_attn(int mode, int dtype, int head_dim, int block, const AttnP
                        hipStream_t stream);
 
 // Query rows per workgroup of a bf16 attention pass.  The dense passes at
-// D = 128 use 256 rows (8 waves, one workgroup per CU): every K/V tile then
-// feeds twice the rows, halving the L2 traffic per flop (measured 2-3 %
-// faster).  Sparse attention stays at 128 rows: its workgroup walks the
-// union of its query blocks' lists, which is ~3 % longer than each list for
-// two 64-token blocks and ~8 % for four.  A sparse work item -- and a
-// launch-plan entry -- covers this many rows of one (batch, head).
-constexpr int attn_rows(int mode, int head_dim, int block) {
-  return ((mode == kDense || mode == kDenseMass) && head_dim == 128 && block <= 128) ? 256 : 128;
+// D = 128 that write lse (and the one-sweep construction) use 256 rows (8
+// waves, one workgroup per CU): every K/V tile then feeds twice the rows,
+// halving the L2 traffic per flop (measured 2-3 % faster).  Dense attention
+// without lse runs the 128-row lean pass of sparse attention (attn_bf16.hip)
+// and takes the same time.  Sparse attention stays at 128 rows: its
+// workgroup walks the union of its query blocks' lists, which is ~3 % longer
+// than each list for two 64-token blocks and ~8 % for four.  A sparse work
+// item -- and a launch-plan entry -- covers this many rows of one (batch,
+// head).
+constexpr int attn_rows(int mode, int head_dim, int block, bool lse = true) {
+  return (((mode == kDense && lse) || mode == kDenseMass) && head_dim == 128 && block <= 128)
+             ? 256
+             : 128;
 }
 
 // bf16 kernels (LDS-DMA pipeline); same contract as launch_attn.
