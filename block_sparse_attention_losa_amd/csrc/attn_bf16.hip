@@ -33,23 +33,23 @@
 //    so that both the K fragment reads (ds_read_b128) and the transposing V
 //    reads (ds_read_b64_tr_b16, which hand each lane four keys of one head
 //    dim) are free of bank conflicts;
-//  * K runs one tile ahead of V: the scores of tile t+1 are computed on the
-//    matrix cores while tile t's softmax runs on the VALU, and the loads of
-//    K(t+2) and V(t+1) are in flight during both.  The D = 128 sparse pass
-//    with lse, the mass pass and the D = 64 dense pass with lse issue those
-//    score MFMAs inside the softmax block, interleaved with the
+//  * in the dense passes with lse, the one-sweep construction at D = 128 and
+//    the two passes of the mass map, K runs one tile ahead of V: the scores
+//    of tile t+1 are computed on the matrix cores while tile t's softmax
+//    runs on the VALU, and the loads of K(t+2) and V(t+1) are in flight
+//    during both.  The mass pass and the D = 64 dense pass with lse issue
+//    those score MFMAs inside the softmax block, interleaved with the
 //    exponentials; the other prefetching 128-row passes issue them ahead of
 //    it at a lower wave priority, so the two waves of a SIMD (from different
 //    workgroups) tend to alternate between the matrix core and the VALU;
-//  * except in the "lean" passes (lean_pass: at D = 64 every pass with a
-//    P V product but dense attention with lse, at D = 128 sparse and dense
-//    attention without lse): there K and V both run one tile ahead, a tile's
-//    scores are computed in its own step, a wave skips the tiles its block
-//    did not keep, and at D = 64 the 32 registers this saves give four
-//    waves per SIMD instead of three; the lean passes without lse take row
-//    maxima only on a wave's first kept tile and keep that reference, with
-//    a second walk over the tiles for a workgroup whose sums leave the fp32
-//    range.
+//  * the "lean" passes (lean_pass: sparse attention, dense attention without
+//    lse, the one-sweep construction at D = 64) run K and V both one tile
+//    ahead and compute a tile's scores in its own step; a wave skips the
+//    tiles its block did not keep, and at D = 64 the 32 registers this
+//    saves give four waves per SIMD instead of three.  The lean passes
+//    without lse take row maxima only on a wave's first kept tile and keep
+//    that reference, with a second walk over the tiles for a workgroup
+//    whose sums leave the fp32 range.
 //
 // Scores are computed transposed, S^T = K Q^T, on 32x32x16 MFMA tiles: a
 // lane then holds one query row and 16 of the 32 keys of a chunk, so row
@@ -94,8 +94,8 @@ struct GeoB {
 
 // "Lean" passes compute a tile's scores at the start of its own step instead
 // of one step ahead, and a wave skips outright the tiles its query block did
-// not keep.  At D = 64 -- sparse attention (with or without lse), dense
-// attention without lse and the one-sweep construction -- this frees the 32
+// not keep.  At D = 64 -- sparse attention, dense attention without lse and
+// the one-sweep construction -- this frees the 32
 // registers of the second score set and the loop fits 128 VGPRs: four waves
 // per SIMD.  A score there carries half the matrix work of D = 128 and the
 // same softmax work, so the loop is bound by latency and VALU issue rather
@@ -110,10 +110,12 @@ struct GeoB {
 // consume) no per-tile row maxima; measured 3.6-3.7 % faster on the
 // Wan2.1-1.3B and HunyuanVideo layers than the prefetching form, and the
 // 128-row lean dense pass within 0.3 % of the 256-row prefetching one, so
-// sparse attention over every block stays bit-identical to it.
+// sparse attention over every block stays bit-identical to it.  Sparse
+// attention with lse (the drift diagnostic) runs lean too, with fp32 row sums
+// and the row maxima of every tile: the same arithmetic per tile as the
+// dense pass with lse, so bit-identical to it over every block.
 constexpr bool lean_pass(int d, int mode, bool mfsum) {
-  return (d == 64 && (mode == kSparse || (mode == kDense && mfsum) || mode == kDenseMass)) ||
-         (d == 128 && (mode == kSparse || mode == kDense) && mfsum);
+  return mode == kSparse || (mode == kDense && mfsum) || (d == 64 && mode == kDenseMass);
 }
 
 // Workgroups per CU the register budget is sized for.  Two waves per SIMD at
@@ -213,7 +215,6 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
   auto key0_of = [&](int t) -> int {
     return (entry_at(t) & 0xFFFF) * BLK + (G::kSubs == 1 ? 0 : (t & 1) * 64);
   };
-  auto member = [&](int t) -> bool { return ((entry_at(t) >> (16 + qi)) & 1) != 0; };
 
   // ---- LDS ring: K tiles at slots 0/1, V tiles at slots 2/3
   unsigned char* kslot[2] = {smem, smem + G::kTileBytes};
@@ -377,22 +378,13 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
     return __builtin_bit_cast(bf16x8, wv);
   };
 
-  // Sparse at D = 128 with lse: the next tile's score MFMAs are issued inside
-  // the softmax block (after the rare raise branch), where the scheduler
-  // interleaves them with the exponentials.  That needs the softmax on every
-  // tile of the union, so a wave whose query block did not keep the tile
-  // runs it against an exponent reference of +inf -- exact zero
-  // probabilities, no raise, P V adds nothing, the same bits -- instead of
-  // branching around it.  The union exceeds each list by ~3 %; measured
-  // 0.7 % faster than the branch with the score MFMAs at a lower wave
-  // priority.  (The sparse passes at D = 64, and at D = 128 without lse,
-  // run lean instead, see lean_pass; at D = 64 issued inline, the two score
-  // sets spill heavily at three waves per SIMD.)  The mass pass (no P V, every wave keeps every
-  // tile) and the D = 64 dense pass with lse (128-row workgroups) issue them
-  // the same way: 1-2 % faster, the same bits.  (The 256-row dense passes
-  // measured within noise, the D = 64 dense+mass pass 9 % slower.)
-  constexpr bool kInline =
-      (MODE == kSparse && D == 128) || MODE == kMass || (MODE == kDense && D == 64 && !kLean);
+  // The mass pass (no P V) and the D = 64 dense pass with lse (128-row
+  // workgroups) issue the next tile's score MFMAs inside the softmax block
+  // (after the rare raise branch), where the scheduler interleaves them with
+  // the exponentials: 1-2 % faster than issuing them ahead of it at a lower
+  // wave priority, the same bits.  (The 256-row dense passes measured within
+  // noise, the D = 64 dense+mass pass 9 % slower.)
+  constexpr bool kInline = MODE == kMass || (MODE == kDense && D == 64 && !kLean);
 
   // keys past the sequence end score -inf (a final tile that runs past N)
   auto mask_tail = [&](f32x16 (&sc)[2], int key0) {
@@ -417,11 +409,9 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
   };
 
   // softmax of tile t (scores in sc) and its P V product; with kInline also
-  // the scores of the next tile (K in nslot) into sn, with kSpecExp nslot is
-  // the tile's own K (for a recompute).  keep is false for a tile this
-  // wave's query block did not keep (kInline only).
+  // the scores of the next tile (K in nslot) into sn
   auto consume = [&](int t, int key0, f32x16 (&sc)[2], auto masked,
-                     const unsigned char* nslot, f32x16 (&sn)[2], bool keep) {
+                     const unsigned char* nslot, f32x16 (&sn)[2]) {
     if constexpr (decltype(masked)::value) mask_tail(sc, key0);
     if constexpr (MODE == kMass) {
       compute_s(nslot, sn);
@@ -500,7 +490,7 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[cc][i]);
       mx = pair_max(mx);
-      const float m_cand = keep ? mx * c2 : -INFINITY;
+      const float m_cand = mx * c2;
       const bool raise = m_cand > m_thr;
       const bool any_raise = __ballot(raise) != 0;
       float alpha = 1.0f;
@@ -523,7 +513,7 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
         if constexpr (kMfmaSum) lacc[0] *= alpha;
       }
       if constexpr (kInline) compute_s(nslot, sn);
-      const float m_e = keep ? m_use : INFINITY;
+      const float m_e = m_use;
       // with the row sums on the matrix cores the exponentials are taken
       // where the P V product packs them (fewer live registers: at D = 64
       // this removes the loop's spills)
@@ -658,7 +648,7 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
         __builtin_amdgcn_s_setprio(0);
         compute_s(kslot[t & 1], sc);
         __builtin_amdgcn_s_setprio(1);
-        consume(t, key0, sc, masked, kslot[t & 1], sn, true);
+        consume(t, key0, sc, masked, kslot[t & 1], sn);
       }
       wait_dma_all();
       __syncthreads();
@@ -680,25 +670,15 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
     // MFMAs) and the other in its score MFMAs, the softmax issues first and
     // the score MFMAs fill its stalls (measured: 1-3 % faster than equal
     // priorities).
-    if constexpr (kInline && MODE != kSparse) {
-      consume(t, key0, sc, masked, kslot[(t + 1) & 1], sn, true);
-    } else if constexpr (kInline) {
-      consume(t, key0, sc, masked, kslot[(t + 1) & 1], sn, ((e0 >> (16 + qi)) & 1) != 0);
-    } else if constexpr (MODE == kSparse) {
-      // waves skip the softmax and P V of tiles their query block did not
-      // keep; the next tile's scores are computed regardless (the union
-      // exceeds each list by ~3 %), which keeps that work branch-free
-      if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
-      compute_s(kslot[(t + 1) & 1], sn);
-      if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
-      if (((e0 >> (16 + qi)) & 1) != 0) consume(t, key0, sc, masked, nullptr, sn, true);
+    if constexpr (kInline) {
+      consume(t, key0, sc, masked, kslot[(t + 1) & 1], sn);
     } else {
       // scores of the next tile; after the last tile this reads a stale
       // slot and the result is dropped, which keeps the block branch-free
       if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
       compute_s(kslot[(t + 1) & 1], sn);
       if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
-      consume(t, key0, sc, masked, nullptr, sn, true);
+      consume(t, key0, sc, masked, nullptr, sn);
     }
     wait_dma_all();
     __syncthreads();
@@ -725,10 +705,8 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
     if (ntile > 0) {
       wait_dma_all();
       __syncthreads();
-      // (with kInline every wave runs the softmax of tile 0, so its scores
-      // must be real numbers even where the wave's block did not keep it)
       if (!kLean) {
-        if (MODE != kSparse || kInline || member(0)) compute_s(kslot[0], sa);
+        compute_s(kslot[0], sa);
         __syncthreads();  // K slot 0 may be refilled from here on
       }
     }
