@@ -3,6 +3,14 @@
 Usage: ``python -m block_sparse_attention_losa_amd.build`` (or call
 :func:`build`).  Every call recompiles.
 
+``python -m block_sparse_attention_losa_amd.build --lds-poison`` builds the
+LDS-poison debug library, ``liblosa_poison.so`` beside ``liblosa.so``: the
+same sources with ``LOSA_LDS_POISON`` defined, so that the attention kernels
+fill their LDS with NaN bit patterns before each walk over the tiles and
+before every tile slot is refilled (attn_common.h).  A GPU test runs the
+path through both libraries and requires the same output bits.  It is a
+checking build, never the product.
+
 ``python -m block_sparse_attention_losa_amd.build --host-sanitizers``
 builds instead a CPU-side test library, ``_build/asan/liblosa_asan.so``:
 the host code of every source with AddressSanitizer and
@@ -55,6 +63,40 @@ def _compile(src: str) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     return obj
+
+
+POISON_DIR = os.path.join(OBJ_DIR, "poison")
+POISON_LIB = os.path.join(PKG, "liblosa_poison.so")
+
+
+def _compile_poison(src: str) -> str:
+    obj = os.path.join(POISON_DIR, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + COMMON + ["-DLOSA_LDS_POISON"]
+    if src.endswith(".hip"):
+        cmd += ["-x", "hip", f"--offload-arch={ARCH}"] + DEVICE_FLAGS
+    else:
+        cmd += ["-D__HIP_PLATFORM_AMD__"]
+    cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    return obj
+
+
+def build_poison(verbose: bool = False) -> str:
+    """The LDS-poison debug library (see the module doc)."""
+    os.makedirs(POISON_DIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+        objs = list(ex.map(_compile_poison, HIP_SOURCES + HOST_SOURCES))
+    tmp = POISON_LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, POISON_LIB)
+    if verbose:
+        print(f"built {POISON_LIB}")
+    return POISON_LIB
 
 
 ASAN_DIR = os.path.join(OBJ_DIR, "asan")
@@ -125,6 +167,8 @@ def build(verbose: bool = False) -> str:
 if __name__ == "__main__":
     if "--host-sanitizers" in sys.argv[1:]:
         build_sanitized(verbose=True)
+    elif "--lds-poison" in sys.argv[1:]:
+        build_poison(verbose=True)
     else:
         build(verbose=True)
     sys.exit(0)

@@ -153,6 +153,7 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
   }
   // padding of the XCD-aware grid; a plan entry outside the items is ignored
   if (item < 0 || item >= wph * bh_count) return;
+  LOSA_POISON(G::kThreads, smem, G::lds_bytes(nb));  // debug build only
   const int bh = item / wph;
   const int w = item - bh * wph;
   const size_t head_off =
@@ -641,6 +642,8 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
       // priorities here too)
       if (t + 1 < ntile) {
         const int k1 = kHave ? key0_from(e1, t + 1) : key0_of(t + 1);
+        LOSA_POISON(G::kThreads, kslot[(t + 1) & 1], G::kTileBytes);  // debug build only
+        LOSA_POISON(G::kThreads, vslot[(t + 1) & 1], G::kTileBytes);
         dma_tile(kh, k1, kslot[(t + 1) & 1], koff);
         dma_tile(vh, k1, vslot[(t + 1) & 1], voff);
       }
@@ -657,12 +660,16 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
     flush_rowsum();
     // loads for later tiles: K(t+2) into the K slot freed by tile t, V(t+1)
     // into the V slot freed by tile t-1
-    if (t + 2 < ntile)
+    if (t + 2 < ntile) {
+      LOSA_POISON(G::kThreads, kslot[t & 1], G::kTileBytes);  // debug build only
       dma_tile(kh, kHave ? key0_from(e2, t + 2) : key0_of(t + 2), kslot[t & 1], koff);
+    }
     if constexpr (G::kWithV)
-      if (t + 1 < ntile)
+      if (t + 1 < ntile) {
+        LOSA_POISON(G::kThreads, vslot[(t + 1) & 1], G::kTileBytes);
         dma_tile(vh, kHave ? key0_from(e1, t + 1) : key0_of(t + 1),
                  vslot[(t + 1) & 1], voff);
+      }
     // Wave priority (kPrio): the next tile's score MFMAs issue
     // at the lowest level, everything else (softmax, P V, loads, the
     // barrier) one above.  The two waves sharing a SIMD come from different
@@ -691,6 +698,7 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
   if constexpr (kSpecExp)
     if (tid == 0) *redo_word = 0;  // ordered before any use by the barriers below
   for (;;) {
+    LOSA_POISON(G::kThreads, smem, G::kRingBytes);  // debug build only: the tile ring
     if (ntile > 0) {
       dma_tile(kh, key0_of(0), kslot[0], koff);
       if constexpr (G::kWithV) dma_tile(vh, key0_of(0), vslot[0], voff);

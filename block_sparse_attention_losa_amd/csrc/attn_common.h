@@ -54,6 +54,27 @@ __device__ __forceinline__ v4i16 ds_read_tr16(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
 }
 
+// LDS poisoning, compiled in only for the debug build (LOSA_LDS_POISON):
+// every thread of the workgroup fills bytes (a multiple of 16) of LDS at p
+// with all-ones words -- NaN as fp32 and as bf16, -1 as an index -- and the
+// workgroup then meets at a barrier.  The attention kernels poison all of
+// their LDS at the start of each walk over the tiles and every tile slot
+// before a load refills it, so that a read of LDS no load or store wrote
+// since (a missing wait, a wrong slot, a row past the tile) puts NaN in the
+// outputs instead of a stale value that looks plausible.  In other builds
+// LOSA_POISON expands to nothing, so their code is untouched.
+#ifdef LOSA_LDS_POISON
+template <int kThreads>
+__device__ __forceinline__ void lds_poison(unsigned char* p, int bytes) {
+  const u32x4 ones = {~0u, ~0u, ~0u, ~0u};
+  for (int j = threadIdx.x; j < bytes / 16; j += kThreads) ((u32x4*)p)[j] = ones;
+  __syncthreads();
+}
+#define LOSA_POISON(threads, p, bytes) lds_poison<threads>((p), (bytes))
+#else
+#define LOSA_POISON(threads, p, bytes) ((void)0)
+#endif
+
 // Union of the frozen lists of up to kQPW query blocks, ascending, written
 // to list[] as (block | member_bits << 16); returns its length.  Called by
 // all kThreads threads of the workgroup; nb <= kMaxLen.
