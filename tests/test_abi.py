@@ -187,12 +187,12 @@ def test_per_row_select_mask_and_retained_validation(lib):
 def test_sparse_plan_validation(lib):
     d = desc(batch=1, heads=12, seq_len=32760, block=64)
     # a 4-word header, then one slot per 128-row work item, padded to whole
-    # rounds of 8 runs of 8
+    # rounds of 8 runs (one per XCD) of 16 items
     assert lib.losa_sparse_plan_size(d) == 4 * (4 + 12 * 256)
     assert lib.losa_sparse_plan_size(desc(seq_len=118800, block=128, heads=24)) == \
-        4 * (4 + 22336)
+        4 * (4 + 128 * ((24 * 929 + 127) // 128))
     assert lib.losa_sparse_plan_size(desc(batch=2, heads=48, seq_len=17776, head_dim=64)) \
-        == 4 * (4 + 64 * ((2 * 48 * 139 + 63) // 64))
+        == 4 * (4 + 128 * ((2 * 48 * 139 + 127) // 128))
     assert lib.losa_sparse_plan_size(None) == -1
     need = lib.losa_sparse_plan_size(d)
     assert lib.losa_sparse_plan(d, NULL, FAKE, need, NULL) == 1

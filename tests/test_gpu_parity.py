@@ -78,7 +78,7 @@ CASES = {
 def _check_plan(plan, count, blk):
     """A plan opens with a header naming its shape (magic, work items, nb,
     query blocks per item), then places every work item (one per 128 query
-    rows of each (b, h)) exactly once; read in rank order (runs of 8 ranks
+    rows of each (b, h)) exactly once; read in rank order (runs of 16 ranks
     per XCD, dealt to the 8 XCDs in turn), the cost buckets never rise and
     items of one bucket keep their index order.  Unused slots hold -1."""
     b, h, nb = count.shape
@@ -89,7 +89,7 @@ def _check_plan(plan, count, blk):
     plan = plan[4:]
     assert np.array_equal(np.sort(plan[plan >= 0]), np.arange(n))
     assert (plan[plan < 0] == -1).all()
-    ch, xcds = 8, 8
+    ch, xcds = 16, 8
     slots = np.arange(len(plan))
     x, within = slots % xcds, slots // xcds
     rank = ((within // ch) * xcds + x) * ch + within % ch
@@ -448,7 +448,7 @@ def test_scale_argument(losa):
 
 def test_plan_of_another_shape_is_not_followed(losa):
     """A plan made for another shape with the same number of slots (8 work
-    items of two heads against 12 of three, both 64 slots) passes the size
+    items of two heads against 12 of three, both 128 slots) passes the size
     check; its header names the other shape, so the kernel runs every work
     item in index order instead of the plan's slots: the same bits as the
     unplanned call, every row written, within the bounds of the oracle."""
