@@ -88,7 +88,10 @@ __global__ void __launch_bounds__(256) retained_mass_kernel(const float* __restr
 // within 3 % of the balanced bound; sorting by exact cost reaches 1 % but
 // scatters each head's query blocks and doubled the K/V traffic.  Runs of
 // 16 fetch 9 % fewer bytes per sparse call than runs of 8 at the same
-// time; runs of 32 fetch 17 % fewer but cost 1 % on the Wan2.1-1.3B layer.)
+// time; runs of 32 fetch 17 % fewer but cost 1 % on the Wan2.1-1.3B layer,
+// and dealing runs of 24-64 in alternating XCD order with 8 cost buckets
+// fetches 22-40 % fewer at 0.3-5 % more time: the kernel is not bound by
+// memory, so fewer fetched bytes do not make it faster.)
 constexpr int kPlanBuckets = 32;
 constexpr int kPlanChunk = 16;
 
