@@ -11,9 +11,10 @@
 //    denoising steps (ubos.tech blog, "Key Findings"; aitobox blog, "Key
 //    Highlights"); R measures that on the caller's own inputs;
 //  * sparse_plan_kernel -- a dispatch order for the sparse kernel, made once
-//    per set of frozen lists: the work items ranked by descending cost and
-//    dealt to the XCDs so that every XCD gets the same mix of long and short
-//    items and runs its longest ones first (layout below).
+//    per set of frozen lists: the work items ranked by descending cost, in
+//    runs of neighbouring query blocks assigned to the XCDs so that every
+//    XCD gets the same summed cost and runs its longest items first (layout
+//    below).
 //    Per-head kept fractions range from a few percent to all blocks, and in
 //    the default head-major order the last items to start are often long
 //    ones, leaving the chip part-idle at the end.
@@ -74,55 +75,62 @@ __global__ void __launch_bounds__(256) retained_mass_kernel(const float* __restr
 }
 
 // Plan layout (after the header that names the shape, losa_launch.h).
-// Items are ranked by cost, descending, in kPlanBuckets
-// buckets (cost * kPlanBuckets / (nb + 1)); within a bucket they keep their
-// index order (head-major, query blocks ascending), so runs of consecutive
-// ranks are neighbouring query blocks of one head, whose lists overlap.
-// Runs of kPlanChunk ranks go to one XCD, runs dealt to the 8 XCDs in turn:
-// rank s -> chunk c = s / kPlanChunk, XCD x = c % 8, round r = c / 8, and
-// slot 8 * (r * kPlanChunk + s % kPlanChunk) + x, which the hardware hands
-// to XCD x as its (r * kPlanChunk + s % kPlanChunk)-th workgroup.  Every XCD
-// thus gets the same mix of costs, longest first, and the workgroups
-// resident on an XCD mostly share one head's K/V.  Slots past the last item
-// hold -1.  (On the Wan2.1-1.3B lists this keeps the simulated makespan
-// within 3 % of the balanced bound; sorting by exact cost reaches 1 % but
-// scatters each head's query blocks and doubled the K/V traffic.  Runs of
-// 16 fetch 9 % fewer bytes per sparse call than runs of 8 at the same
-// time; runs of 32 fetch 17 % fewer but cost 1 % on the Wan2.1-1.3B layer,
-// and dealing runs of 24-64 in alternating XCD order with 8 cost buckets
-// fetches 22-40 % fewer at 0.3-5 % more time: the kernel is not bound by
-// memory, so fewer fetched bytes do not make it faster.)
+// Items are ranked by cost, descending, in kPlanBuckets buckets (cost *
+// kPlanBuckets / (nb + 1), cost = the larger count of the item's query
+// blocks); within a bucket they keep their index order (head-major, query
+// blocks ascending), so a run of kPlanChunk consecutive ranks holds
+// neighbouring query blocks of one head, whose lists overlap.  Each run
+// goes to one XCD: taken in rank order, a run is assigned to the XCD with
+// the least summed cost so far among those with room for another (every
+// XCD takes at most ceil(runs / 8) runs; ties to the lower XCD), a run's
+// cost being the sum over its items of max(cost, 1).  An XCD runs its runs
+// in the order it received them, longest first: run p of XCD x fills slots
+// 8 * (p * kPlanChunk + i) + x, i < kPlanChunk, which the hardware hands to
+// XCD x as its (p * kPlanChunk + i)-th workgroup.  Slots no item reaches
+// hold -1.  With more than kPlanMaxRuns runs (LDS), run c is dealt to XCD
+// c % 8 instead, at position c / 8.
+// (Against dealing every plan's runs in turn: 0.2-0.85 % faster on the
+// Wan2.1-1.3B layer on three boxes and 0.7-0.9 % on the CogVideoX layer.
+// Exact cost sorting balanced slightly better but scattered each head's
+// query blocks and doubled the K/V traffic.  Runs of 16 fetch 9 % fewer
+// bytes per sparse call than runs of 8 at the same time; runs of 32 fetch
+// 17 % fewer but cost 1 % on the Wan2.1-1.3B layer, and dealing runs of
+// 24-64 in alternating XCD order with 8 cost buckets fetches 22-40 % fewer
+// at 0.3-5 % more time: the kernel is not bound by memory, so fewer
+// fetched bytes do not make it faster.)
 constexpr int kPlanBuckets = 32;
 constexpr int kPlanChunk = 16;
+constexpr int kPlanMaxRuns = 4096;
 
 __host__ __device__ inline long long plan_slots(long long n_items) {
   const long long chunks = (n_items + kPlanChunk - 1) / kPlanChunk;
   return (long long)kXcds * kPlanChunk * ((chunks + kXcds - 1) / kXcds);
 }
 
-__device__ __forceinline__ int plan_slot(int s) {
-  const int c = s / kPlanChunk;
-  return kXcds * ((c / kXcds) * kPlanChunk + s % kPlanChunk) + c % kXcds;
-}
-
-// One workgroup of 1024 threads: a stable counting sort of the items by
-// bucket (histogram, then tiles of 1024 items in index order, ranks within a
-// tile from wave ballots), written straight to the slots.  Deterministic.
+// One workgroup of 1024 threads.  The ranking is a stable counting sort by
+// bucket (histogram, then tiles of 1024 items in index order, ranks within
+// a tile from wave ballots).  It runs twice: first to sum each run's cost,
+// then, after one wave has assigned the runs to the XCDs, to write every
+// item to its slot.  Deterministic.
 __global__ void __launch_bounds__(1024) sparse_plan_kernel(const int32_t* __restrict__ count,
                                                            int nb, int qpw, int n_items, int wph,
                                                            int32_t* __restrict__ order) {
   __shared__ int start[kPlanBuckets];       // next rank of each bucket
+  __shared__ int start0[kPlanBuckets];      // first rank of each bucket
   __shared__ int wcnt[16][kPlanBuckets];    // per-wave bucket counts of a tile
+  __shared__ int run_cost[kPlanMaxRuns];
+  __shared__ int run_slot[kPlanMaxRuns];    // position on its XCD * 8 + XCD
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  auto bucket_of = [&](int item) -> int {
+  auto cost_of = [&](int item) -> int {
     const int bh = item / wph;
     const int w = item - bh * wph;
     const int q0 = w * qpw;
     int c = 0;
     for (int q = q0; q < min(nb, q0 + qpw); ++q)
       c = max(c, min(max(count[(size_t)bh * nb + q], 0), nb));
-    return min(kPlanBuckets - 1, c * kPlanBuckets / (nb + 1));
+    return c;
   };
+  auto bucket_of = [&](int c) -> int { return min(kPlanBuckets - 1, c * kPlanBuckets / (nb + 1)); };
   if (tid == 0) {
     order[0] = kPlanMagic;
     order[1] = n_items;
@@ -130,51 +138,91 @@ __global__ void __launch_bounds__(1024) sparse_plan_kernel(const int32_t* __rest
     order[3] = qpw;
   }
   order += kPlanHeader;
+  const int n_runs = (n_items + kPlanChunk - 1) / kPlanChunk;
+  const bool balance = n_runs <= kPlanMaxRuns;
   if (tid < kPlanBuckets) start[tid] = 0;
+  if (balance)
+    for (int r = tid; r < n_runs; r += 1024) run_cost[r] = 0;
+  const int slots = (int)plan_slots(n_items);
+  for (int j = tid; j < slots; j += 1024) order[j] = -1;  // items overwrite theirs below
   __syncthreads();
-  for (int item = tid; item < n_items; item += 1024) atomicAdd(&start[bucket_of(item)], 1);
+  for (int item = tid; item < n_items; item += 1024) atomicAdd(&start[bucket_of(cost_of(item))], 1);
   __syncthreads();
   if (tid == 0) {  // exclusive prefix, most expensive bucket first
     int run = 0;
     for (int k = kPlanBuckets - 1; k >= 0; --k) {
       const int h = start[k];
       start[k] = run;
+      start0[k] = run;
       run += h;
     }
   }
-  // slots of the last round that no rank reaches
-  const int slots = (int)plan_slots(n_items);
-  for (int j = tid; j < kXcds * kPlanChunk; j += 1024) {
-    const int slot = slots - kXcds * kPlanChunk + j;
-    const int x = slot % kXcds, within = slot / kXcds;
-    const int s_rank = ((within / kPlanChunk) * kXcds + x) * kPlanChunk + within % kPlanChunk;
-    if (s_rank >= n_items) order[slot] = -1;
-  }
   __syncthreads();
-  for (int base = 0; base < n_items; base += 1024) {
-    const int item = base + tid;
-    const int bkt = item < n_items ? bucket_of(item) : -1;
-    const unsigned long long below = lane ? ((~0ull) >> (64 - lane)) : 0ull;
-    int rank = 0;
-    for (int k = 0; k < kPlanBuckets; ++k) {
-      const unsigned long long m = __ballot(bkt == k);
-      if (bkt == k) rank = __popcll(m & below);
-      if (lane == 0) wcnt[wave][k] = __popcll(m);
+  // fn(item, cost, rank) for every item, ranks in the order described above
+  auto rank_items = [&](auto&& fn) {
+    for (int base = 0; base < n_items; base += 1024) {
+      const int item = base + tid;
+      const int c = item < n_items ? cost_of(item) : 0;
+      const int bkt = item < n_items ? bucket_of(c) : -1;
+      const unsigned long long below = lane ? ((~0ull) >> (64 - lane)) : 0ull;
+      int rank = 0;
+      for (int k = 0; k < kPlanBuckets; ++k) {
+        const unsigned long long m = __ballot(bkt == k);
+        if (bkt == k) rank = __popcll(m & below);
+        if (lane == 0) wcnt[wave][k] = __popcll(m);
+      }
+      __syncthreads();
+      if (bkt >= 0) {
+        int s_rank = start[bkt] + rank;
+        for (int w2 = 0; w2 < wave; ++w2) s_rank += wcnt[w2][bkt];
+        fn(item, c, s_rank);
+      }
+      __syncthreads();
+      if (tid < kPlanBuckets) {
+        int add = 0;
+        for (int w2 = 0; w2 < 16; ++w2) add += wcnt[w2][tid];
+        start[tid] += add;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (bkt >= 0) {
-      int s_rank = start[bkt] + rank;
-      for (int w2 = 0; w2 < wave; ++w2) s_rank += wcnt[w2][bkt];
-      order[plan_slot(s_rank)] = item;
-    }
-    __syncthreads();
-    if (tid < kPlanBuckets) {
-      int add = 0;
-      for (int w2 = 0; w2 < 16; ++w2) add += wcnt[w2][tid];
-      start[tid] += add;
-    }
-    __syncthreads();
+  };
+  if (!balance) {
+    rank_items([&](int item, int, int s) {
+      const int c = s / kPlanChunk;
+      order[kXcds * ((c / kXcds) * kPlanChunk + s % kPlanChunk) + c % kXcds] = item;
+    });
+    return;
   }
+  rank_items([&](int, int c, int s) { atomicAdd(&run_cost[s / kPlanChunk], max(c, 1)); });
+  if (wave == 0) {
+    // lane x < 8 keeps XCD x's summed cost and run count; per run, the
+    // smallest (cost * 8 + x) over the XCDs with room picks the XCD.  The
+    // next run's cost is read a step ahead, and the update has no branch, so
+    // the step's dependency chain is the DPP minimum alone
+    const int cap = (n_runs + kXcds - 1) / kXcds;
+    int load = 0, taken = 0;
+    int rc = n_runs > 0 ? run_cost[0] : 0;
+    for (int r = 0; r < n_runs; ++r) {
+      const int rc_next = r + 1 < n_runs ? run_cost[r + 1] : 0;
+      int v = (lane < kXcds && taken < cap) ? load * kXcds + lane : 0x7FFFFFFF;
+      v = min(v, row_xor<1>(v));
+      v = min(v, row_xor<2>(v));
+      v = min(v, row_xor<4>(v));
+      const int x = __builtin_amdgcn_readfirstlane(v) & (kXcds - 1);
+      const int tk = __builtin_amdgcn_readlane(taken, x);
+      if (lane == 0) run_slot[r] = tk * kXcds + x;
+      const bool mine = lane == x;
+      load += mine ? rc : 0;
+      taken += mine ? 1 : 0;
+      rc = rc_next;
+    }
+  }
+  if (tid < kPlanBuckets) start[tid] = start0[tid];
+  __syncthreads();
+  rank_items([&](int item, int, int s) {
+    const int rs = run_slot[s / kPlanChunk];
+    order[kXcds * ((rs / kXcds) * kPlanChunk + s % kPlanChunk) + rs % kXcds] = item;
+  });
 }
 
 long long sparse_plan_slots(long long n_items) { return plan_slots(n_items); }

@@ -75,32 +75,55 @@ CASES = {
 }
 
 
-def _check_plan(plan, count, blk):
-    """A plan opens with a header naming its shape (magic, work items, nb,
-    query blocks per item), then places every work item (one per 128 query
-    rows of each (b, h)) exactly once; read in rank order (runs of 16 ranks
-    per XCD, dealt to the 8 XCDs in turn), the cost buckets never rise and
-    items of one bucket keep their index order.  Unused slots hold -1."""
+def _expected_plan(count, blk):
+    """The launch plan the library must produce, built here from its
+    description: a header naming the shape (magic, work items, nb, query
+    blocks per item); the work items (one per 128 query rows of each (b, h))
+    ranked by cost bucket, descending, index order within a bucket (cost =
+    the larger clipped count of the item's query blocks, bucket =
+    cost * 32 // (nb + 1)); runs of 16 ranks assigned in rank order to the
+    XCD with the least summed cost (sum of max(cost, 1)) among those with
+    room for another run (ceil(runs / 8) each; ties to the lower XCD) -- or,
+    beyond 4096 runs, run c to XCD c % 8 at position c // 8; run p of XCD x
+    in slots 8 * (16 p + i) + x; every other slot -1."""
     b, h, nb = count.shape
     qpw = 2 if blk == 64 else 1
     wph = (nb + qpw - 1) // qpw
     n = b * h * wph
-    assert plan[:4].tolist() == [0x41536F4C, n, nb, qpw]
-    plan = plan[4:]
-    assert np.array_equal(np.sort(plan[plan >= 0]), np.arange(n))
-    assert (plan[plan < 0] == -1).all()
-    ch, xcds = 16, 8
-    slots = np.arange(len(plan))
-    x, within = slots % xcds, slots // xcds
-    rank = ((within // ch) * xcds + x) * ch + within % ch
-    items = plan[np.argsort(rank)]
-    items = items[items >= 0]
-    flat = count.reshape(b * h, nb)
-    cost = np.array([flat[i // wph, (i % wph) * qpw:(i % wph) * qpw + qpw].max() for i in items])
+    flat = np.clip(count.reshape(b * h, nb), 0, nb)
+    cost = np.array([flat[i // wph, (i % wph) * qpw:(i % wph) * qpw + qpw].max() for i in range(n)],
+                    dtype=np.int64).reshape(-1)
     bucket = np.minimum(31, cost * 32 // (nb + 1))
-    assert (np.diff(bucket) <= 0).all()
-    same = np.diff(bucket) == 0
-    assert (np.diff(items)[same] > 0).all()
+    ranked = sorted(range(n), key=lambda i: (-bucket[i], i))
+    ch, xcds = 16, 8
+    n_runs = -(-n // ch)
+    cap = -(-n_runs // xcds)
+    plan = np.full(4 + xcds * ch * cap, -1, np.int64)
+    plan[:4] = [0x41536F4C, n, nb, qpw]
+    if n_runs <= 4096:
+        load, taken, run_slot = [0] * xcds, [0] * xcds, []
+        for r in range(n_runs):
+            rc = sum(max(int(cost[i]), 1) for i in ranked[r * ch:(r + 1) * ch])
+            x = min((xx for xx in range(xcds) if taken[xx] < cap), key=lambda xx: (load[xx], xx))
+            run_slot.append((taken[x], x))
+            load[x] += rc
+            taken[x] += 1
+    else:
+        run_slot = [(r // xcds, r % xcds) for r in range(n_runs)]
+    for s_, item in enumerate(ranked):
+        p_, x = run_slot[s_ // ch]
+        plan[4 + xcds * (p_ * ch + s_ % ch) + x] = item
+    return plan
+
+
+def _check_plan(plan, count, blk):
+    """Every slot of the library's plan equals the one built from the
+    description (and so places every work item exactly once)."""
+    expect = _expected_plan(count, blk)
+    assert plan.shape == expect.shape
+    assert np.array_equal(plan.astype(np.int64), expect)
+    items = expect[4:]
+    assert np.array_equal(np.sort(items[items >= 0]), np.arange(expect[1]))
 
 
 def _compare_attention(o_gpu, lse_gpu, o_ref, lse_ref, what):
@@ -476,3 +499,35 @@ def test_plan_of_another_shape_is_not_followed(losa):
     for h in range(cfg.heads):
         ro, rl = oracle.sparse_attention(q[0, h], k[0, h], v[0, h], ig[0, h], cg[0, h], 64)
         _compare_attention(og[0, h], lg[0, h], ro, rl, f"foreign plan h{h}")
+
+
+PLAN_SHAPES = [  # (B, H, nb, block, fill): counts drawn per query block
+    (1, 3, 5, 64, "random"), (2, 3, 17, 64, "random"), (1, 4, 9, 128, "random"),
+    (1, 12, 512, 64, "random"), (1, 2, 40, 64, "zero"), (1, 2, 40, 64, "full"),
+    (1, 256, 512, 64, "random"),   # 65536 items: 4096 runs, the most balanced
+    (1, 300, 512, 64, "random"),   # 4800 runs: dealt to the XCDs in turn
+]
+
+
+@pytest.mark.parametrize("b,h,nb,blk,fill", PLAN_SHAPES)
+def test_plan_matches_its_description(losa, b, h, nb, blk, fill):
+    """The launch plan, slot by slot, against one built on the host from its
+    description (cost ranking, runs assigned to the least-loaded XCD with
+    room, the in-turn dealing beyond 4096 runs), on counts alone."""
+    _say(f"[parity] plan B{b} H{h} nb{nb} block{blk} {fill}")
+    rng = np.random.default_rng(b * 1000 + h * 10 + nb)
+    if fill == "zero":
+        cnt = np.zeros((b, h, nb), np.int32)
+    elif fill == "full":
+        cnt = np.full((b, h, nb), nb, np.int32)
+    else:
+        # per head a kept fraction, per query block a count around it, and a
+        # few entries outside [0, nb] (clipped by the plan)
+        frac = rng.uniform(0.02, 1.0, size=(b, h, 1))
+        cnt = np.clip(np.round(frac * nb * rng.uniform(0.5, 1.5, size=(b, h, nb))), 0, nb)
+        cnt = cnt.astype(np.int32)
+        cnt.reshape(-1)[rng.integers(0, cnt.size, size=4)] = [-3, nb + 5, 0, nb]
+    tc = torch.from_numpy(cnt).to("cuda")
+    plan = losa.sparse_plan(tc, block=blk, head_dim=128)
+    torch.cuda.synchronize()
+    _check_plan(plan.cpu().numpy(), cnt, blk)
