@@ -137,9 +137,10 @@ __global__ void __launch_bounds__((ROWS * 2), attn_occupancy(D, MODE, ROWS, MFSU
   const int bh_count = p.items / nb;
   const int wph = (nb + G::kQPW - 1) / G::kQPW;  // workgroups per (batch, head)
   // a plan (sparse only) gives the item of each workgroup directly: items
-  // ranked by descending cost and dealt to the XCDs in runs of neighbouring
-  // query blocks, so every XCD gets the same mix and starts with its longest
-  // items (layout in frozen_lists.hip); -1 marks an unused slot.  A plan
+  // ranked by descending cost and assigned to the XCDs in runs of
+  // neighbouring query blocks, so every XCD gets the same summed cost and
+  // starts with its longest items (layout in frozen_lists.hip); -1 marks an
+  // unused slot.  A plan
   // whose header names another shape is not followed: the workgroups then
   // take the items in index order (the grid has a slot for each), so every
   // row is still written

@@ -257,13 +257,14 @@ losa_status losa_sparse_attn(const losa_attn_desc* desc, const void* q, const vo
  * "Abstract (arXiv)": index freezing; legiblepapers, FAQ Q6), and neither
  * does the work they imply, so the order in which the GPU should run it can
  * be fixed once too: per-head kept fractions range from a few percent to
- * every block, and running the work items longest-first, dealt evenly over
- * the chip's 8 XCDs, keeps all compute units busy to the end.
+ * every block, and running the work items longest-first, in runs of
+ * neighbouring query blocks spread over the chip's 8 XCDs so that each XCD
+ * gets the same summed cost, keeps all compute units busy to the end.
  * losa_sparse_plan writes that order (int32, losa_sparse_plan_size(desc)
  * bytes, 4-byte aligned, caller-owned) from count [B,H,nb]; only count is
  * read.  Recompute it whenever count changes.  Returns LOSA_ERR_WORKSPACE
- * when plan_bytes is below the size.  Items of equal cost may be ordered
- * differently from call to call; results do not depend on the order.  The
+ * when plan_bytes is below the size.  The same counts give the same plan;
+ * results do not depend on the order.  The
  * plan opens with a header naming the shape it was made for (work items,
  * nb, query blocks per item).
  * losa_sparse_attn_planned computes exactly what losa_sparse_attn computes
